@@ -1,0 +1,308 @@
+"""Benchmark of the packed-QKV split + per-head RMSNorm + RoPE path on one MI355X.
+
+One step = one training layer of the Qwen3-8B-like sectioned workload at
+T = 16384 tokens: ``qkvnr_forward`` (split, q/k RMSNorm, RoPE, v copy) then
+``qkvnr_backward`` (inverse RoPE, RMSNorm backward, packed dqkv, norm-weight
+grads), bf16, inputs resident in HBM.  ``value`` is algorithmic bytes per step
+(each input byte read once, each output byte written once; the backward's
+re-read of the packed input counts) divided by the step's wall time: HBM GB/s.
+
+Cache hygiene: MI355X has a 256 MB Infinity Cache and one step touches
+~0.97 GB.  Three buffer sets rotate: step i runs the forward on set i mod 3 and
+the backward on set (i - 1) mod 3 (a batch whose forward ran a step earlier,
+as in a model where other layers run between a layer's forward and backward),
+so no read finds data left in the cache by the previous ~0.97 GB of traffic.
+
+Also reported (``extras``): Muse-Spark decode at T = 1/8/64/256 (HIP-graph
+replays, us per call), Muse prefill at T = 16384 as a RoPE and a NoPE layer
+(us, GB/s), the MLA latent paged store (us), and the CPU oracle on a bounded
+sample of the step's workload (``cpu_baseline``).
+
+Prints one JSON line.  Only one GPU: ``--gpus`` above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "qkv split+norm+RoPE µs/layer & HBM GB/s (% peak): T=16k fwd+bwd, T=1 decode"
+KERNEL_SOURCES = ["qkv_split_head_amd/csrc/kernels.h", "qkv_split_head_amd/csrc/device.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_gqa_bf16_d128_train16k_traffic.txt")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def gqa_bytes(T, n_q, n_kv, D, es, rope=True):
+    """Algorithmic bytes: forward reads the packed row and writes q/k/v; backward reads
+    the q/k slots of the packed row, dq/dk/dv, and writes the packed dqkv."""
+    row = (n_q + 2 * n_kv) * D * es
+    fwd = 2 * row * T
+    bwd = ((n_q + n_kv) * D * es + 2 * row) * T
+    return fwd, bwd
+
+
+def traffic_from_profile():
+    """HBM bytes per backward launch from the committed rocprofv3 counter summary, or None
+    if it is missing or was taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(target_s: float = 12.0):
+    """Oracle (NumPy fp64, single thread) on the step's workload, token chunks until ~target_s."""
+    import oracle
+    from qkv_inputs import train_sectioned
+
+    w = train_sectioned(2048)
+    fwd_b, bwd_b = gqa_bytes(1, 32, 8, 128, 2)
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        sl = slice(done % w.T, done % w.T + 256)
+        oracle.forward_gqa(w.qkv[sl], "bf16", "sectioned", 8, 4, 128, w.positions[sl], w.q_norm_w, w.k_norm_w,
+                           w.eps, w.theta)
+        oracle.backward_gqa(w.qkv[sl], "bf16", "sectioned", 8, 4, 128, w.positions[sl], w.q_norm_w,
+                            w.k_norm_w, w.eps, w.theta, w.dq[sl], w.dk[sl], w.dv[sl])
+        done += 256
+        el = time.perf_counter() - t0
+        if el >= target_s:
+            break
+    return {
+        "value": round((fwd_b + bwd_b) * done / el / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{done} tokens of the same workload (sectioned 32q/8kv/D128 bf16, fwd+bwd) in "
+                  f"{el:.1f} s on one host core (NumPy fp64, single-threaded ufuncs); "
+                  f"{el / done * 16384 * 1e3:.0f} ms per 16384-token layer",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-extras", action="store_true", help="only the training step")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import qkv_split_head_amd as qk
+    from qkv_inputs import decode_interleaved, latent_paged, prefill_interleaved, train_sectioned
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    dev = "cuda"
+
+    def dev_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ---------------------------------------------------------------- training step (T = 16k)
+    T, n_q, n_kv, D = 16384, 32, 8, 128
+    w = train_sectioned(T)
+    base = dict(qkv=dev_bf16(w.qkv), dq=dev_bf16(w.dq), dk=dev_bf16(w.dk), dv=dev_bf16(w.dv))
+    pos = torch.from_numpy(w.positions).to(dev)
+    wq, wk = dev_bf16(w.q_norm_w), dev_bf16(w.k_norm_w)
+    del w
+    sets = []
+    for i in range(3):
+        s = {k: (v if i == 0 else v.clone()) for k, v in base.items()}
+        s["q"] = torch.empty((T, n_q, D), dtype=torch.bfloat16, device=dev)
+        s["k"] = torch.empty((T, n_kv, D), dtype=torch.bfloat16, device=dev)
+        s["v"] = torch.empty((T, n_kv, D), dtype=torch.bfloat16, device=dev)
+        s["dqkv"] = torch.empty_like(s["qkv"])
+        s["dwq"] = torch.empty(D, dtype=torch.float32, device=dev)
+        s["dwk"] = torch.empty(D, dtype=torch.float32, device=dev)
+        sets.append(s)
+    kw = dict(kind="sectioned", n_kv=n_kv, q_per_kv=n_q // n_kv, head_dim=D, eps=1e-6, theta=1e6)
+
+    def fwd(s):
+        qk.forward(s["qkv"], pos, wq, wk, out=(s["q"], s["k"], s["v"]), **kw)
+
+    def bwd(s):
+        qk.backward(s["qkv"], pos, wq, wk, s["dq"], s["dk"], s["dv"], out=(s["dqkv"], s["dwq"], s["dwk"]), **kw)
+
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        fwd(sets[i % 3])
+        bwd(sets[(i - 1) % 3])
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        fwd(sets[i % 3])
+        ev[i][1].record(stream)
+        bwd(sets[(i - 1) % 3])
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]))
+    bwd_ms = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]))
+    fwd_b, bwd_b = gqa_bytes(T, n_q, n_kv, D, 2)
+    ms_per_step = wall / K * 1e3
+    value = (fwd_b + bwd_b) / (ms_per_step * 1e-3) / 1e9
+    bwd_gbs = bwd_b / (bwd_ms * 1e-3) / 1e9
+    traffic = traffic_from_profile()
+    del sets, base
+
+    extras = {
+        "train_fwd_us": round(fwd_ms * 1e3, 2),
+        "train_fwd_GBps": round(fwd_b / (fwd_ms * 1e-3) / 1e9, 1),
+        "train_bwd_us": round(bwd_ms * 1e3, 2),
+        "train_bwd_GBps": round(bwd_gbs, 1),
+        "train_step_us_events": round((fwd_ms + bwd_ms) * 1e3, 2),
+        "train_algorithmic_bytes": {"fwd": fwd_b, "bwd": bwd_b},
+    }
+
+    if not args.no_extras:
+        # ------------------------------------------------------------ Muse prefill, RoPE and NoPE layers
+        for rope in (True, False):
+            pw = prefill_interleaved(16384, rope=rope)
+            pq = dev_bf16(pw.qkv)
+            pp = torch.from_numpy(pw.positions).to(dev)
+            pwq, pwk = dev_bf16(pw.q_norm_w), dev_bf16(pw.k_norm_w)
+            pk = dict(kind="interleaved", n_kv=16, q_per_kv=8, head_dim=64, rope=rope, eps=1e-6, theta=5e5)
+            bufs = [(pq if i == 0 else pq.clone()) for i in range(2)]
+            outs = [(torch.empty((16384, 128, 64), dtype=torch.bfloat16, device=dev),
+                     torch.empty((16384, 16, 64), dtype=torch.bfloat16, device=dev),
+                     torch.empty((16384, 16, 64), dtype=torch.bfloat16, device=dev)) for _ in range(2)]
+            for i in range(4):
+                qk.forward(bufs[i % 2], pp, pwq, pwk, out=outs[i % 2], **pk)
+            n = 20
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(n):
+                qk.forward(bufs[i % 2], pp, pwq, pwk, out=outs[i % 2], **pk)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / n * 1e3
+            pb, _ = gqa_bytes(16384, 128, 16, 64, 2)
+            tag = "rope" if rope else "nope"
+            extras[f"prefill_{tag}_us"] = round(us, 2)
+            extras[f"prefill_{tag}_GBps"] = round(pb / (us * 1e-6) / 1e9, 1)
+            del bufs, outs, pq
+
+        # ------------------------------------------------------------ decode, HIP-graph replays
+        for Td in (1, 8, 64, 256):
+            dw = decode_interleaved(Td)
+            dq_ = dev_bf16(dw.qkv)
+            dp = torch.from_numpy(dw.positions).to(dev)
+            dwq_, dwk_ = dev_bf16(dw.q_norm_w), dev_bf16(dw.k_norm_w)
+            o = (torch.empty((Td, 128, 64), dtype=torch.bfloat16, device=dev),
+                 torch.empty((Td, 16, 64), dtype=torch.bfloat16, device=dev),
+                 torch.empty((Td, 16, 64), dtype=torch.bfloat16, device=dev))
+            dk_ = dict(kind="interleaved", n_kv=16, q_per_kv=8, head_dim=64, eps=1e-6, theta=5e5)
+            side = torch.cuda.Stream()
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                for _ in range(3):
+                    qk.forward(dq_, dp, dwq_, dwk_, out=o, **dk_)
+            stream.wait_stream(side)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                qk.forward(dq_, dp, dwq_, dwk_, out=o, **dk_)
+            for _ in range(10):
+                g.replay()
+            n = 200
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(n):
+                g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            extras[f"decode_T{Td}_us"] = round(e0.elapsed_time(e1) / n * 1e3, 2)
+            del g
+
+        # ------------------------------------------------------------ MLA latent rows into the paged pool
+        lw = latent_paged()
+        rows, lp, lwk = dev_bf16(lw.qkv), torch.from_numpy(lw.positions).to(dev), dev_bf16(lw.k_norm_w)
+        bt = torch.from_numpy(lw.block_table).to(dev)
+        pool = torch.zeros((lw.num_pages, lw.page_size, 576), dtype=torch.bfloat16, device=dev)
+        for _ in range(3):
+            qk.forward_latent_paged(rows, lp, lwk, bt, pool, tokens_per_req=lw.tokens_per_req)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            qk.forward_latent_paged(rows, lp, lwk, bt, pool, tokens_per_req=lw.tokens_per_req)
+        n = 200
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        extras["mla_latent_paged_B4xT16_us"] = round(e0.elapsed_time(e1) / n * 1e3, 2)
+        del pool, g
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "us_per_layer": round(ms_per_step * 1e3, 2),
+        "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBS, 1),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(1,0.1) norm weights)",
+        "config": {
+            "workload": "Qwen3-8B-like training layer, sectioned packed qkv [16384, (32+8+8)*128] bf16, "
+                        "q/k RMSNorm + RoPE theta 1e6, forward + backward",
+            "tokens": T, "n_q": n_q, "n_kv": n_kv, "head_dim": D, "layout": "sectioned",
+            "buffer_sets_rotated": 3,
+        },
+        "roofline": {
+            "kernel": "bwd_gqa_kernel<bf16, D=128, RoPE> (+ its weight-grad zeroing launch)",
+            "bound": "hbm",
+            "achieved": round(bwd_gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(bwd_gbs / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+        },
+        "extras": extras,
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

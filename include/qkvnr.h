@@ -1,0 +1,201 @@
+/*
+ * qkvnr — packed-QKV split + per-head RMSNorm + RoPE for MI355X (gfx950).
+ *
+ * C ABI of the library libqkvnr.so.  Plain pointers and sizes only.
+ *
+ * What the entry points compute (sources are the three public pages this
+ * library is built from):
+ *   - torchtitan "[muse_spark][perf] Split the packed qkv inside the q/k
+ *     region": Problem items 1-4 and Solution items 1-3 with the before/after
+ *     diagram.  The fused projection's packed output is split into q, k and v;
+ *     q and k get a per-head RMSNorm with a learned weight and then RoPE (no
+ *     rotation on NoPE layers); v is copied; the backward writes one packed
+ *     grad directly, with no concatenation of three grads.
+ *   - DeepSpeed "[muon] Per-head Newton-Schulz for fused QKV projections",
+ *     "What this PR does": the two fused layouts (sectioned and interleaved per
+ *     KV group), each a partition of the row into n_q + 2*n_kv head blocks of
+ *     head_dim values, and the exact-total guard that declines any other width.
+ *   - TensorRT-LLM "MLA DSpark: run each drafter layer's kv path beside its q
+ *     path", Description: the latent kv row's RMSNorm/RoPE kernel stores its
+ *     result straight into the paged context pool at the block table's
+ *     page/offset, bitwise what a staged buffer plus a scatter would write.
+ *
+ * Definitions (per token t at position p = positions[t]):
+ *   RMSNorm of a head x[0..D):  y_d = x_d * w_d / sqrt(mean_d(x_d^2) + eps)
+ *   RoPE, rotate-half, R = rotated width, i < R/2, phi_i = p * theta^(-2i/R):
+ *     y_i       = x_i cos(phi_i) - x_{i+R/2} sin(phi_i)
+ *     y_{i+R/2} = x_{i+R/2} cos(phi_i) + x_i sin(phi_i)
+ *   The angle is taken as the real number p * theta^(-2i/R): the kernels form it
+ *   in fp64 and reduce it in turns, so large positions (>= 1e5) keep full
+ *   accuracy.  Arithmetic is fp32; each output is rounded once (nearest-even).
+ *
+ * Conventions common to every entry point:
+ *   - All pointers are device pointers (HIP device memory), owned by the
+ *     caller.  The library never allocates, frees or keeps a pointer after it
+ *     returns.  Outputs must not overlap inputs.
+ *   - Work is enqueued on `stream` (0 = the default stream); a return value of
+ *     QKVNR_OK means "enqueued", not "finished".  Faults inside a kernel
+ *     surface at the caller's next synchronisation, as for any HIP launch.
+ *   - Every argument is validated on the host before any HIP call is made; a
+ *     negative return code means nothing was enqueued.
+ *   - Tensors of activations use the layout's dtype (bf16 or fp32), the norm
+ *     weights too.  Norm-weight gradients are fp32.  positions are int32.
+ *   - Every tensor pointer (except positions, block tables and fp32 weight
+ *     gradients, which need 4-byte alignment) must be 16-byte aligned, and the
+ *     packed input's row stride in bytes must be a multiple of 16.
+ *   - T == 0 is valid: nothing is read or written and every tensor pointer may
+ *     be NULL, except that the backward still zeroes the norm-weight
+ *     gradients, whose pointers must then be valid.
+ *   - Calls on one stream are ordered; calls that overlap on different streams
+ *     and write the same memory race, as for any kernel.
+ */
+#ifndef QKVNR_H
+#define QKVNR_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QKVNR_VERSION 10000 /* major * 10000 + minor * 100 + patch */
+
+/* Return codes. */
+#define QKVNR_OK 0
+#define QKVNR_EINVAL (-1)      /* a null pointer, a bad size, or a width that is not the exact total */
+#define QKVNR_EALIGN (-2)      /* a pointer or the input row stride is not aligned as required */
+#define QKVNR_EUNSUPPORTED (-3)/* a shape this build has no kernel for, or no gfx950 device current */
+#define QKVNR_EHIP (-4)        /* a HIP runtime call or launch failed; qkvnr_strerror has its text */
+
+/* Packed layouts. */
+#define QKVNR_INTERLEAVED 0 /* [T, n_kv, q_per_kv + 2, head_dim]: per kv group q..., k, v */
+#define QKVNR_SECTIONED 1   /* [T, (n_q + 2 n_kv) * head_dim]: n_q q heads, n_kv k, n_kv v */
+#define QKVNR_LATENT 2      /* [T, norm_dim + rope_dim]: one MLA latent row per token */
+
+/* Storage dtypes. */
+#define QKVNR_BF16 0
+#define QKVNR_FP32 1
+
+/*
+ * Layout descriptor of the packed input.
+ *
+ *   kind          QKVNR_INTERLEAVED, QKVNR_SECTIONED or QKVNR_LATENT.
+ *   dtype         QKVNR_BF16 or QKVNR_FP32 (LATENT: BF16 only).
+ *   T             tokens (rows); 0 <= T < 2^31.
+ *   n_kv          kv heads = kv groups (GQA kinds), >= 1.  Ignored for LATENT.
+ *   q_per_kv      q heads per kv group (GQA kinds), >= 1; n_q = n_kv * q_per_kv.
+ *                 Ignored for LATENT.
+ *   head_dim      D, 64 or 128 (GQA kinds).  Ignored for LATENT.
+ *   rope_dim      GQA kinds: 0 (NoPE layer: no rotation, positions unused) or
+ *                 head_dim (rotate the whole head).  LATENT: 64, the rotated
+ *                 tail of the row.
+ *   norm_dim      LATENT only: 512, the normalised head of the row.
+ *   width         elements of the packed row.  Must equal exactly
+ *                 (n_q + 2 n_kv) * head_dim for the GQA kinds and
+ *                 norm_dim + rope_dim for LATENT (the exact-total guard);
+ *                 any other width is QKVNR_EINVAL.
+ *   in_row_stride elements from one token's packed row to the next, >= width.
+ *                 The backward writes dqkv with the same row stride (elements
+ *                 of a row beyond `width` are not touched).
+ */
+typedef struct qkvnr_layout {
+  int32_t kind;
+  int32_t dtype;
+  int64_t T;
+  int32_t n_kv;
+  int32_t q_per_kv;
+  int32_t head_dim;
+  int32_t rope_dim;
+  int32_t norm_dim;
+  int32_t reserved;
+  int64_t width;
+  int64_t in_row_stride;
+} qkvnr_layout;
+
+/*
+ * Forward: split, per-head RMSNorm of q and k, RoPE of q and k (unless
+ * rope_dim == 0), copy of v, contiguous outputs.
+ * (torchtitan page: Problem items 1-3, Solution items 1 and 3, diagram "after".
+ *  TensorRT-LLM page: Description, the latent RMSNorm/RoPE before its store.)
+ *
+ * GQA kinds:
+ *   qkv        packed input, `layout` describes it.
+ *   positions  [T] int32, 0 <= p < 2^31; may be NULL when rope_dim == 0.
+ *   q_norm_w   [head_dim] weight shared by every q head.
+ *   k_norm_w   [head_dim] weight shared by every k head.
+ *   eps        added to the mean square inside the square root; >= 0, finite.
+ *   theta      RoPE base, > 0 and finite when rope_dim > 0.
+ *   q          out [T, n_q, head_dim]; q head h = g * q_per_kv + s for slot s of group g.
+ *   k, v       out [T, n_kv, head_dim]; v is a bit-exact copy of the v slots.
+ * LATENT kind:
+ *   q_norm_w, q and v must be NULL; k_norm_w is the [norm_dim] weight;
+ *   k is out [T, norm_dim + rope_dim]: [RMSNorm(row[0:norm_dim]) || RoPE(row[norm_dim:])].
+ */
+int qkvnr_forward(const qkvnr_layout* layout, const void* qkv, const int32_t* positions,
+                  const void* q_norm_w, const void* k_norm_w, float eps, double theta,
+                  void* q, void* k, void* v, hipStream_t stream);
+
+/*
+ * Backward of qkvnr_forward for the GQA kinds: inverse RoPE of the incoming
+ * grads, then the RMSNorm backward, written as one packed grad in the input's
+ * layout (no concatenation), plus the norm-weight grads.
+ * (torchtitan page: Problem item 4, Solution item 3, diagram "after".)
+ *
+ *   qkv, positions, q_norm_w, k_norm_w, eps, theta: as given to the forward
+ *              (the backward recomputes the norm statistics from qkv).
+ *   dq         [T, n_q, head_dim], dk and dv [T, n_kv, head_dim]: grads of the outputs.
+ *   dqkv       out, packed like qkv (row stride in_row_stride); its v slots are
+ *              a bit-exact copy of dv.
+ *   dq_norm_w  out [head_dim] fp32, dk_norm_w out [head_dim] fp32: overwritten
+ *              (zeroed on `stream`, then accumulated with fp32 atomics, so the
+ *              last bits may differ from run to run).
+ * LATENT is QKVNR_EUNSUPPORTED.
+ */
+int qkvnr_backward(const qkvnr_layout* layout, const void* qkv, const int32_t* positions,
+                   const void* q_norm_w, const void* k_norm_w, float eps, double theta,
+                   const void* dq, const void* dk, const void* dv, void* dqkv,
+                   float* dq_norm_w, float* dk_norm_w, hipStream_t stream);
+
+/*
+ * Forward that stores k and v (GQA kinds) or the latent row (LATENT) straight
+ * into a paged pool at the block table's page/offset, instead of a contiguous
+ * buffer that is scattered afterwards.  Same arithmetic as qkvnr_forward, only
+ * the store index differs, so the pool rows are bitwise what qkvnr_forward
+ * followed by a scatter would write.
+ * (TensorRT-LLM page: Description, the direct pool write; Test Coverage, the
+ *  bitwise comparison with the staged write.)
+ *
+ *   block_table    [ceil(T / tokens_per_req), bt_stride] int32 page ids.
+ *   tokens_per_req tokens per request: token t belongs to request t / tokens_per_req.
+ *   page_size      rows per page, P >= 1.
+ *   num_pages      pages in the pool.
+ *   Token t at position p goes to page block_table[b][p / P], row p % P of it.
+ *   A token whose p / P >= bt_stride, or whose page id is outside
+ *   [0, num_pages), is not stored (its pool rows are left as they were); the
+ *   caller should treat that as an error in its own table.
+ * GQA kinds:
+ *   q       out [T, n_q, head_dim], contiguous as in qkvnr_forward.
+ *   k_pool  [num_pages, page_size, n_kv, head_dim]; v_pool likewise.
+ * LATENT kind:
+ *   q_norm_w, q and v_pool must be NULL; k_norm_w is the [norm_dim] weight;
+ *   k_pool is [num_pages, page_size, norm_dim + rope_dim].
+ */
+int qkvnr_forward_paged(const qkvnr_layout* layout, const void* qkv, const int32_t* positions,
+                        const void* q_norm_w, const void* k_norm_w, float eps, double theta,
+                        const int32_t* block_table, int32_t bt_stride, int32_t tokens_per_req,
+                        int32_t page_size, int32_t num_pages, void* q, void* k_pool,
+                        void* v_pool, hipStream_t stream);
+
+/* Static text for a return code.  For QKVNR_EHIP and the validation errors it
+ * returns the last detailed message recorded on the calling thread. */
+const char* qkvnr_strerror(int code);
+
+/* QKVNR_VERSION of the built library. */
+int qkvnr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QKVNR_H */

@@ -14,6 +14,7 @@ from .generators import (  # noqa: F401
     prefill_interleaved,
     train_sectioned,
     latent_paged,
+    gqa_paged,
     custom_gqa,
     SEEDS,
 )

@@ -177,28 +177,14 @@ def train_sectioned(T: int = 16384, grads: bool = True) -> Workload:
                       name=f"qwen3_8b_train_T{T}")
 
 
-def latent_paged(
-    B: int = 4,
-    T_req: int = 16,
-    num_pages: int = 8192,
-    page_size: int = 64,
-    norm_dim: int = 512,
-    rope_dim: int = 64,
-    ctx_lo: int = 2048,
-    ctx_hi: int = 131072,
-    seed: int = SEEDS["latent"],
-) -> Workload:
-    """MLA-style latent rows [B*T_req, 512+64] bf16 and a random non-overlapping block table.
+def _block_table(rng, B, T_req, num_pages, page_size, ctx_lo, ctx_hi):
+    """Context lengths, draft-token positions and a non-overlapping block table.
 
     Draft token i of request b sits at position ``ctx_b + i``.  Request b owns
     ``ceil((ctx_b + T_req) / page_size)`` distinct pages taken in order from one
     seeded permutation of all pages; unused table entries are -1.  Context
-    lengths are redrawn (deterministically, same generator) until the pages fit.
+    lengths are redrawn (same generator) until the pages fit in the pool.
     """
-    rng = np.random.Generator(np.random.PCG64(seed))
-    T = B * T_req
-    rows = _draw(rng, (T, norm_dim + rope_dim), "bf16")
-    w = _draw(rng, (norm_dim,), "bf16", 1.0, 0.1)
     bt_stride = -(-(ctx_hi + T_req) // page_size)
     while True:
         ctx = rng.integers(ctx_lo, ctx_hi, size=B, endpoint=True, dtype=np.int64)
@@ -213,10 +199,62 @@ def latent_paged(
         n = int(need[b])
         table[b, :n] = perm[at:at + n]
         at += n
+    return ctx, pos, table
+
+
+def latent_paged(
+    B: int = 4,
+    T_req: int = 16,
+    num_pages: int = 8192,
+    page_size: int = 64,
+    norm_dim: int = 512,
+    rope_dim: int = 64,
+    ctx_lo: int = 2048,
+    ctx_hi: int = 131072,
+    seed: int = SEEDS["latent"],
+) -> Workload:
+    """MLA-style latent rows [B*T_req, 512+64] bf16 and a random non-overlapping block table."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    T = B * T_req
+    rows = _draw(rng, (T, norm_dim + rope_dim), "bf16")
+    w = _draw(rng, (norm_dim,), "bf16", 1.0, 0.1)
+    ctx, pos, table = _block_table(rng, B, T_req, num_pages, page_size, ctx_lo, ctx_hi)
     return Workload(
         name=f"mla_latent_paged_B{B}_T{T_req}", kind="latent", dtype="bf16", T=T,
         n_kv=1, q_per_kv=0, head_dim=norm_dim + rope_dim, rope_dim=rope_dim,
         eps=1e-6, theta=1e4, qkv=rows, positions=pos, q_norm_w=None, k_norm_w=w,
         norm_dim=norm_dim, block_table=table, tokens_per_req=T_req,
+        page_size=page_size, num_pages=num_pages, extra={"ctx": ctx},
+    )
+
+
+def gqa_paged(
+    kind: str,
+    dtype: str,
+    B: int,
+    T_req: int,
+    n_kv: int,
+    q_per_kv: int,
+    head_dim: int,
+    *,
+    num_pages: int = 256,
+    page_size: int = 16,
+    ctx_lo: int = 0,
+    ctx_hi: int = 2000,
+    rope: bool = True,
+    theta: float = 1e4,
+    seed: int = 0,
+) -> Workload:
+    """GQA batch whose k/v go to paged pools: B requests of T_req tokens after random contexts."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    T = B * T_req
+    qkv = _draw(rng, _packed_shape(kind, T, n_kv, q_per_kv, head_dim), dtype)
+    wq = _draw(rng, (head_dim,), dtype, 1.0, 0.1)
+    wk = _draw(rng, (head_dim,), dtype, 1.0, 0.1)
+    ctx, pos, table = _block_table(rng, B, T_req, num_pages, page_size, ctx_lo, ctx_hi)
+    return Workload(
+        name=f"gqa_paged_{kind}_{dtype}_B{B}_T{T_req}", kind=kind, dtype=dtype, T=T, n_kv=n_kv,
+        q_per_kv=q_per_kv, head_dim=head_dim, rope_dim=head_dim if rope else 0, eps=1e-6, theta=theta,
+        qkv=qkv, positions=pos, q_norm_w=wq, k_norm_w=wk, block_table=table, tokens_per_req=T_req,
         page_size=page_size, num_pages=num_pages, extra={"ctx": ctx},
     )

@@ -1,0 +1,35 @@
+"""qkvnr: packed-QKV split + per-head RMSNorm + RoPE on MI355X (gfx950).
+
+Python face of ``libqkvnr.so`` (C ABI in ``include/qkvnr.h``).  The functions
+named like the C entry points (``qkvnr_forward``, ``qkvnr_backward``,
+``qkvnr_forward_paged``) pass tensors straight through; ``forward``,
+``backward``, ``forward_paged``, ``forward_latent`` and
+``forward_latent_paged`` also allocate the outputs.
+"""
+from ._binding import (  # noqa: F401
+    BF16,
+    EALIGN,
+    EHIP,
+    EINVAL,
+    EUNSUPPORTED,
+    FP32,
+    INTERLEAVED,
+    LATENT,
+    OK,
+    SECTIONED,
+    Layout,
+    QkvnrError,
+    backward,
+    forward,
+    forward_latent,
+    forward_latent_paged,
+    forward_paged,
+    gqa_layout,
+    header_functions,
+    latent_layout,
+    lib,
+    qkvnr_backward,
+    qkvnr_forward,
+    qkvnr_forward_paged,
+    qkvnr_version,
+)

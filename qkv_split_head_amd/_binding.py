@@ -1,0 +1,232 @@
+"""ctypes binding of libqkvnr.so.
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  torch is used for device memory (allocating outputs) and to name the
+current HIP stream; there is no other code path, and loading fails loudly when
+the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Tuple
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libqkvnr.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "qkvnr.h")
+
+# Mirrors of the header's constants.
+OK, EINVAL, EALIGN, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4
+INTERLEAVED, SECTIONED, LATENT = 0, 1, 2
+BF16, FP32 = 0, 1
+KINDS = {"interleaved": INTERLEAVED, "sectioned": SECTIONED, "latent": LATENT}
+DTYPES = {torch.bfloat16: BF16, torch.float32: FP32}
+
+
+class Layout(ctypes.Structure):
+    """``qkvnr_layout`` of the header."""
+
+    _fields_ = [
+        ("kind", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("T", ctypes.c_int64),
+        ("n_kv", ctypes.c_int32),
+        ("q_per_kv", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("rope_dim", ctypes.c_int32),
+        ("norm_dim", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("width", ctypes.c_int64),
+        ("in_row_stride", ctypes.c_int64),
+    ]
+
+
+class QkvnrError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"qkvnr error {code}: {message}")
+        self.code = code
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it first (python -m qkv_split_head_amd.build); "
+                "there is no fallback implementation")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32p, f32p = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
+        lp = ctypes.POINTER(Layout)
+        L.qkvnr_forward.argtypes = [lp, vp, i32p, vp, vp, ctypes.c_float, ctypes.c_double, vp, vp, vp, vp]
+        L.qkvnr_forward.restype = ctypes.c_int
+        L.qkvnr_backward.argtypes = [lp, vp, i32p, vp, vp, ctypes.c_float, ctypes.c_double, vp, vp, vp, vp,
+                                     f32p, f32p, vp]
+        L.qkvnr_backward.restype = ctypes.c_int
+        L.qkvnr_forward_paged.argtypes = [lp, vp, i32p, vp, vp, ctypes.c_float, ctypes.c_double, i32p,
+                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                          vp, vp, vp, vp]
+        L.qkvnr_forward_paged.restype = ctypes.c_int
+        L.qkvnr_strerror.argtypes = [ctypes.c_int]
+        L.qkvnr_strerror.restype = ctypes.c_char_p
+        L.qkvnr_version.argtypes = []
+        L.qkvnr_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def header_functions() -> list:
+    """Names of the functions ``include/qkvnr.h`` declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(qkvnr_\w+)\s*\(", text, re.M)))
+
+
+def _check(rc: int) -> None:
+    if rc != OK:
+        raise QkvnrError(rc, lib().qkvnr_strerror(rc).decode())
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+# ------------------------------------------------------------------ raw entry points
+
+
+def qkvnr_forward(layout: Layout, qkv, positions, q_norm_w, k_norm_w, eps: float, theta: float, q, k, v,
+                  stream=None) -> None:
+    """Call ``qkvnr_forward``: tensors (or raw device addresses) in, outputs written in place."""
+    _check(lib().qkvnr_forward(ctypes.byref(layout), _ptr(qkv), _ptr(positions), _ptr(q_norm_w), _ptr(k_norm_w),
+                               eps, theta, _ptr(q), _ptr(k), _ptr(v), _stream(stream)))
+
+
+def qkvnr_backward(layout: Layout, qkv, positions, q_norm_w, k_norm_w, eps: float, theta: float, dq, dk, dv,
+                   dqkv, dq_norm_w, dk_norm_w, stream=None) -> None:
+    """Call ``qkvnr_backward``."""
+    _check(lib().qkvnr_backward(ctypes.byref(layout), _ptr(qkv), _ptr(positions), _ptr(q_norm_w), _ptr(k_norm_w),
+                                eps, theta, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dqkv), _ptr(dq_norm_w),
+                                _ptr(dk_norm_w), _stream(stream)))
+
+
+def qkvnr_forward_paged(layout: Layout, qkv, positions, q_norm_w, k_norm_w, eps: float, theta: float,
+                        block_table, bt_stride: int, tokens_per_req: int, page_size: int, num_pages: int,
+                        q, k_pool, v_pool, stream=None) -> None:
+    """Call ``qkvnr_forward_paged``."""
+    _check(lib().qkvnr_forward_paged(ctypes.byref(layout), _ptr(qkv), _ptr(positions), _ptr(q_norm_w),
+                                     _ptr(k_norm_w), eps, theta, _ptr(block_table), bt_stride, tokens_per_req,
+                                     page_size, num_pages, _ptr(q), _ptr(k_pool), _ptr(v_pool), _stream(stream)))
+
+
+def qkvnr_version() -> int:
+    return lib().qkvnr_version()
+
+
+# ------------------------------------------------------------------ tensor-level wrappers
+
+
+def gqa_layout(qkv: torch.Tensor, kind: str, n_kv: int, q_per_kv: int, head_dim: int, rope: bool) -> Layout:
+    """Describe a packed GQA tensor whose rows may be strided but whose row contents are dense."""
+    if qkv.dtype not in DTYPES:
+        raise TypeError(f"qkv dtype {qkv.dtype} is not bf16 or fp32")
+    T = qkv.shape[0]
+    width = (n_kv * q_per_kv + 2 * n_kv) * head_dim
+    if T > 0:
+        if qkv[0].numel() != width:
+            raise ValueError(f"packed row holds {qkv[0].numel()} values, not (n_q + 2 n_kv) * head_dim = {width}")
+        if not qkv[0].is_contiguous():
+            raise ValueError("the values of a packed row must be dense")
+    row_stride = qkv.stride(0) if T > 1 else width
+    return Layout(kind=KINDS[kind], dtype=DTYPES[qkv.dtype], T=T, n_kv=n_kv, q_per_kv=q_per_kv, head_dim=head_dim,
+                  rope_dim=head_dim if rope else 0, norm_dim=0, reserved=0, width=width, in_row_stride=row_stride)
+
+
+def latent_layout(rows: torch.Tensor, norm_dim: int = 512, rope_dim: int = 64) -> Layout:
+    if rows.dim() != 2 or rows.stride(1) != 1:
+        raise ValueError("latent rows must be a 2-D tensor with dense rows")
+    T = rows.shape[0]
+    width = norm_dim + rope_dim
+    return Layout(kind=LATENT, dtype=DTYPES[rows.dtype], T=T, n_kv=1, q_per_kv=0, head_dim=0, rope_dim=rope_dim,
+                  norm_dim=norm_dim, reserved=0, width=width, in_row_stride=rows.stride(0) if T > 1 else width)
+
+
+def forward(qkv: torch.Tensor, positions: Optional[torch.Tensor], q_norm_w: torch.Tensor, k_norm_w: torch.Tensor,
+            *, kind: str, n_kv: int, q_per_kv: int, head_dim: int, rope: bool = True, eps: float = 1e-6,
+            theta: float = 10000.0, out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
+            stream=None):
+    """Split + q/k RMSNorm + RoPE + v copy; returns contiguous (q [T,n_q,D], k [T,n_kv,D], v [T,n_kv,D])."""
+    L = gqa_layout(qkv, kind, n_kv, q_per_kv, head_dim, rope)
+    T = qkv.shape[0]
+    if out is None:
+        q = torch.empty((T, n_kv * q_per_kv, head_dim), dtype=qkv.dtype, device=qkv.device)
+        k = torch.empty((T, n_kv, head_dim), dtype=qkv.dtype, device=qkv.device)
+        v = torch.empty((T, n_kv, head_dim), dtype=qkv.dtype, device=qkv.device)
+    else:
+        q, k, v = out
+    qkvnr_forward(L, qkv, positions, q_norm_w, k_norm_w, eps, theta, q, k, v, stream)
+    return q, k, v
+
+
+def backward(qkv: torch.Tensor, positions: Optional[torch.Tensor], q_norm_w: torch.Tensor, k_norm_w: torch.Tensor,
+             dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor, *, kind: str, n_kv: int, q_per_kv: int,
+             head_dim: int, rope: bool = True, eps: float = 1e-6, theta: float = 10000.0, out=None, stream=None):
+    """Packed dqkv (input layout) and fp32 norm-weight grads (dq_norm_w, dk_norm_w)."""
+    L = gqa_layout(qkv, kind, n_kv, q_per_kv, head_dim, rope)
+    if out is None:
+        dqkv = torch.empty_strided(qkv.shape, qkv.stride(), dtype=qkv.dtype, device=qkv.device)
+        dwq = torch.empty(head_dim, dtype=torch.float32, device=qkv.device)
+        dwk = torch.empty(head_dim, dtype=torch.float32, device=qkv.device)
+    else:
+        dqkv, dwq, dwk = out
+    qkvnr_backward(L, qkv, positions, q_norm_w, k_norm_w, eps, theta, dq, dk, dv, dqkv, dwq, dwk, stream)
+    return dqkv, dwq, dwk
+
+
+def forward_paged(qkv, positions, q_norm_w, k_norm_w, block_table: torch.Tensor, k_pool: torch.Tensor,
+                  v_pool: torch.Tensor, *, kind: str, n_kv: int, q_per_kv: int, head_dim: int,
+                  tokens_per_req: int, rope: bool = True, eps: float = 1e-6, theta: float = 10000.0,
+                  q: Optional[torch.Tensor] = None, stream=None):
+    """GQA forward with k/v stored into pools [num_pages, page_size, n_kv, D]; returns q."""
+    L = gqa_layout(qkv, kind, n_kv, q_per_kv, head_dim, rope)
+    if q is None:
+        q = torch.empty((qkv.shape[0], n_kv * q_per_kv, head_dim), dtype=qkv.dtype, device=qkv.device)
+    num_pages, page_size = k_pool.shape[0], k_pool.shape[1]
+    qkvnr_forward_paged(L, qkv, positions, q_norm_w, k_norm_w, eps, theta, block_table, block_table.shape[1],
+                        tokens_per_req, page_size, num_pages, q, k_pool, v_pool, stream)
+    return q
+
+
+def forward_latent(rows: torch.Tensor, positions: torch.Tensor, norm_w: torch.Tensor, *, eps: float = 1e-6,
+                   theta: float = 10000.0, norm_dim: int = 512, rope_dim: int = 64,
+                   out: Optional[torch.Tensor] = None, stream=None):
+    """Latent rows [T, norm_dim + rope_dim] -> [RMSNorm(head) || RoPE(tail)], contiguous."""
+    L = latent_layout(rows, norm_dim, rope_dim)
+    if out is None:
+        out = torch.empty((rows.shape[0], norm_dim + rope_dim), dtype=rows.dtype, device=rows.device)
+    qkvnr_forward(L, rows, positions, None, norm_w, eps, theta, None, out, None, stream)
+    return out
+
+
+def forward_latent_paged(rows: torch.Tensor, positions: torch.Tensor, norm_w: torch.Tensor,
+                         block_table: torch.Tensor, pool: torch.Tensor, *, tokens_per_req: int,
+                         eps: float = 1e-6, theta: float = 10000.0, norm_dim: int = 512, rope_dim: int = 64,
+                         stream=None) -> None:
+    """Latent rows stored straight into pool [num_pages, page_size, norm_dim + rope_dim]."""
+    L = latent_layout(rows, norm_dim, rope_dim)
+    qkvnr_forward_paged(L, rows, positions, None, norm_w, eps, theta, block_table, block_table.shape[1],
+                        tokens_per_req, pool.shape[1], pool.shape[0], None, pool, None, stream)

@@ -1,0 +1,431 @@
+// Host side of libqkvnr.so: argument validation, launch planning, dispatch.
+//
+// Every check runs on the host before the first HIP call, so a rejected call
+// enqueues nothing and the checks can be exercised on a machine with no GPU.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "kernels.h"
+#include "qkvnr.h"
+
+namespace {
+
+using namespace qkvnr;
+
+thread_local char g_msg[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+// ------------------------------------------------------------------ device
+
+struct DeviceInfo {
+  bool known = false;
+  bool gfx950 = false;
+  int cus = 0;
+};
+constexpr int kMaxDevices = 64;
+DeviceInfo g_devices[kMaxDevices];
+std::mutex g_devices_mu;
+
+// Compute units of the current device, or an error if it is not a gfx950.
+int current_device(int* cus) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(QKVNR_EUNSUPPORTED, "no HIP device is current: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(QKVNR_EUNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_devices_mu);
+  DeviceInfo& d = g_devices[dev];
+  if (!d.known) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(QKVNR_EHIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    d.gfx950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    d.cus = prop.multiProcessorCount;
+    d.known = true;
+  }
+  if (!d.gfx950) return fail(QKVNR_EUNSUPPORTED, "device %d is not gfx950; this library has kernels for gfx950 only", dev);
+  *cus = d.cus;
+  return QKVNR_OK;
+}
+
+int launched(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(QKVNR_EHIP, "%s launch failed: %s", what, hipGetErrorString(e));
+  return QKVNR_OK;
+}
+
+// ------------------------------------------------------------------ validation
+
+int elem_bytes(int32_t dtype) { return dtype == QKVNR_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// Layout checks shared by every entry point.
+int check_layout(const qkvnr_layout* L) {
+  if (!L) return fail(QKVNR_EINVAL, "layout is NULL");
+  if (L->kind != QKVNR_INTERLEAVED && L->kind != QKVNR_SECTIONED && L->kind != QKVNR_LATENT)
+    return fail(QKVNR_EINVAL, "unknown layout kind %d", L->kind);
+  if (L->dtype != QKVNR_BF16 && L->dtype != QKVNR_FP32) return fail(QKVNR_EINVAL, "unknown dtype %d", L->dtype);
+  if (L->T < 0 || L->T > INT32_MAX) return fail(QKVNR_EINVAL, "T = %lld out of [0, 2^31)", (long long)L->T);
+  if (L->kind == QKVNR_LATENT) {
+    if (L->norm_dim <= 0 || L->rope_dim < 0 || (L->rope_dim & 1))
+      return fail(QKVNR_EINVAL, "latent norm_dim %d / rope_dim %d invalid", L->norm_dim, L->rope_dim);
+    if (L->width != static_cast<int64_t>(L->norm_dim) + L->rope_dim)
+      return fail(QKVNR_EINVAL, "latent width %lld != norm_dim + rope_dim = %d", (long long)L->width,
+                  L->norm_dim + L->rope_dim);
+    if (L->dtype != QKVNR_BF16 || L->norm_dim != 512 || L->rope_dim != 64)
+      return fail(QKVNR_EUNSUPPORTED, "latent rows: only bf16 with norm_dim 512 and rope_dim 64 have a kernel");
+  } else {
+    if (L->n_kv < 1 || L->q_per_kv < 1 || L->head_dim < 1)
+      return fail(QKVNR_EINVAL, "n_kv %d, q_per_kv %d, head_dim %d must be >= 1", L->n_kv, L->q_per_kv, L->head_dim);
+    const int64_t n_q = static_cast<int64_t>(L->n_kv) * L->q_per_kv;
+    const int64_t blocks = n_q + 2 * static_cast<int64_t>(L->n_kv);
+    // exact-total guard: the packed width must be (n_q + 2 n_kv) * head_dim
+    if (L->width != blocks * L->head_dim)
+      return fail(QKVNR_EINVAL, "width %lld is not the exact total (n_q + 2 n_kv) * head_dim = %lld",
+                  (long long)L->width, (long long)(blocks * L->head_dim));
+    if (L->rope_dim < 0 || (L->rope_dim & 1) || L->rope_dim > L->head_dim)
+      return fail(QKVNR_EINVAL, "rope_dim %d must be even and in [0, head_dim]", L->rope_dim);
+    if (L->head_dim != 64 && L->head_dim != 128)
+      return fail(QKVNR_EUNSUPPORTED, "head_dim %d: kernels exist for 64 and 128", L->head_dim);
+    if (L->rope_dim != 0 && L->rope_dim != L->head_dim)
+      return fail(QKVNR_EUNSUPPORTED, "rope_dim %d: kernels rotate the whole head (rope_dim = head_dim) or nothing",
+                  L->rope_dim);
+    if (blocks > 65535) return fail(QKVNR_EUNSUPPORTED, "%lld head blocks per token exceed 65535", (long long)blocks);
+  }
+  if (L->in_row_stride < L->width)
+    return fail(QKVNR_EINVAL, "in_row_stride %lld < width %lld", (long long)L->in_row_stride, (long long)L->width);
+  if ((L->in_row_stride * elem_bytes(L->dtype)) % 16 != 0)
+    return fail(QKVNR_EALIGN, "input row stride of %lld bytes is not a multiple of 16",
+                (long long)(L->in_row_stride * elem_bytes(L->dtype)));
+  return QKVNR_OK;
+}
+
+int need16(const void* p, const char* name) {
+  if (!p) return fail(QKVNR_EINVAL, "%s is NULL", name);
+  if (!aligned16(p)) return fail(QKVNR_EALIGN, "%s is not 16-byte aligned", name);
+  return QKVNR_OK;
+}
+
+int need4(const void* p, const char* name) {
+  if (!p) return fail(QKVNR_EINVAL, "%s is NULL", name);
+  if (!aligned4(p)) return fail(QKVNR_EALIGN, "%s is not 4-byte aligned", name);
+  return QKVNR_OK;
+}
+
+int must_be_null(const void* p, const char* name) {
+  if (p) return fail(QKVNR_EINVAL, "%s must be NULL for latent rows", name);
+  return QKVNR_OK;
+}
+
+int check_scalars(const qkvnr_layout* L, float eps, double theta) {
+  if (!std::isfinite(eps) || eps < 0.0f) return fail(QKVNR_EINVAL, "eps %g must be finite and >= 0", (double)eps);
+  if (L->rope_dim > 0 && (!std::isfinite(theta) || !(theta > 0.0)))
+    return fail(QKVNR_EINVAL, "theta %g must be finite and > 0", theta);
+  return QKVNR_OK;
+}
+
+struct Span {
+  const void* p;
+  int64_t bytes;
+};
+
+bool overlaps(Span a, Span b) {
+  if (!a.p || !b.p || a.bytes <= 0 || b.bytes <= 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + static_cast<uintptr_t>(b.bytes) && b0 < a0 + static_cast<uintptr_t>(a.bytes);
+}
+
+int check_disjoint(std::initializer_list<Span> outs, std::initializer_list<Span> ins) {
+  for (const Span& o : outs) {
+    for (const Span& i : ins)
+      if (overlaps(o, i)) return fail(QKVNR_EINVAL, "an output overlaps an input");
+    for (const Span& o2 : outs)
+      if (&o2 != &o && overlaps(o, o2)) return fail(QKVNR_EINVAL, "two outputs overlap");
+  }
+  return QKVNR_OK;
+}
+
+int check_paged(const int32_t* bt, int32_t bt_stride, int32_t tokens_per_req, int32_t page_size, int32_t num_pages) {
+  if (int rc = need4(bt, "block_table")) return rc;
+  if (bt_stride < 1 || tokens_per_req < 1 || page_size < 1 || num_pages < 1)
+    return fail(QKVNR_EINVAL, "bt_stride %d, tokens_per_req %d, page_size %d, num_pages %d must be >= 1", bt_stride,
+                tokens_per_req, page_size, num_pages);
+  return QKVNR_OK;
+}
+
+// ------------------------------------------------------------------ planning
+
+int heads_per_iter(int32_t dtype, int32_t D) { return kWave * (16 / elem_bytes(dtype)) / D; }
+
+// Split tokens into work units and size the grid.  With at least as many tokens
+// as resident waves each unit is a whole token row; with fewer, rows are cut
+// into segments so that small batches (decode) still spread over the chip.
+int plan_gqa(GqaArgs& a, const qkvnr_layout* L, int cus, int blocks_per_cu) {
+  const int hpi = heads_per_iter(L->dtype, L->head_dim);
+  a.n_kv = L->n_kv;
+  a.q_per_kv = L->q_per_kv;
+  a.n_q = L->n_kv * L->q_per_kv;
+  a.heads = a.n_q + 2 * L->n_kv;
+  a.kind = L->kind == QKVNR_INTERLEAVED ? kInterleaved : kSectioned;
+  a.iters = (a.heads + hpi - 1) / hpi;
+  const int64_t target_waves = static_cast<int64_t>(cus) * 16;
+  int64_t seg = a.iters;
+  if (L->T < target_waves) {
+    seg = (static_cast<int64_t>(a.iters) * L->T + target_waves - 1) / target_waves;
+    if (seg < 1) seg = 1;
+  }
+  a.seg_iters = static_cast<int32_t>(seg);
+  a.nseg = (a.iters + a.seg_iters - 1) / a.seg_iters;
+  a.units = L->T * a.nseg;
+  const uint32_t d = static_cast<uint32_t>(a.q_per_kv + 2);
+  a.grp_magic = static_cast<uint32_t>((0x100000000ull + d - 1) / d);
+  a.row_bytes = L->in_row_stride * elem_bytes(L->dtype);
+  a.inv_d = 1.0f / static_cast<float>(L->head_dim);
+  int64_t grid = (a.units + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int64_t cap = static_cast<int64_t>(cus) * blocks_per_cu;
+  if (grid > cap) grid = cap;
+  if (grid < 1) grid = 1;
+  return static_cast<int>(grid);
+}
+
+template <bool PAGED>
+void launch_fwd_gqa(const GqaArgs& a, int32_t dtype, int32_t D, bool rope, int grid, hipStream_t s) {
+  const dim3 g(grid), b(kBlockThreads);
+#define QKVNR_FWD(IO, DD, R) hipLaunchKernelGGL((fwd_gqa_kernel<IO, DD, R, PAGED>), g, b, 0, s, a)
+  if (dtype == QKVNR_BF16) {
+    if (D == 64) { if (rope) QKVNR_FWD(uint16_t, 64, true); else QKVNR_FWD(uint16_t, 64, false); }
+    else         { if (rope) QKVNR_FWD(uint16_t, 128, true); else QKVNR_FWD(uint16_t, 128, false); }
+  } else {
+    if (D == 64) { if (rope) QKVNR_FWD(float, 64, true); else QKVNR_FWD(float, 64, false); }
+    else         { if (rope) QKVNR_FWD(float, 128, true); else QKVNR_FWD(float, 128, false); }
+  }
+#undef QKVNR_FWD
+}
+
+void launch_bwd_gqa(const GqaArgs& a, int32_t dtype, int32_t D, bool rope, int grid, hipStream_t s) {
+  const dim3 g(grid), b(kBlockThreads);
+#define QKVNR_BWD(IO, DD, R) hipLaunchKernelGGL((bwd_gqa_kernel<IO, DD, R>), g, b, 0, s, a)
+  if (dtype == QKVNR_BF16) {
+    if (D == 64) { if (rope) QKVNR_BWD(uint16_t, 64, true); else QKVNR_BWD(uint16_t, 64, false); }
+    else         { if (rope) QKVNR_BWD(uint16_t, 128, true); else QKVNR_BWD(uint16_t, 128, false); }
+  } else {
+    if (D == 64) { if (rope) QKVNR_BWD(float, 64, true); else QKVNR_BWD(float, 64, false); }
+    else         { if (rope) QKVNR_BWD(float, 128, true); else QKVNR_BWD(float, 128, false); }
+  }
+#undef QKVNR_BWD
+}
+
+constexpr int kFwdBlocksPerCu = 8;
+constexpr int kBwdBlocksPerCu = 2;
+
+int latent_forward(const qkvnr_layout* L, const void* qkv, const int32_t* positions, const void* k_norm_w,
+                   float eps, double theta, void* out, int64_t out_bytes, const int32_t* bt, int32_t bt_stride,
+                   int32_t tokens_per_req, int32_t page_size, int32_t num_pages, bool paged, hipStream_t stream) {
+  if (L->T == 0) return QKVNR_OK;  // nothing is read or written
+  if (int rc = need16(qkv, "qkv")) return rc;
+  if (int rc = need4(positions, "positions")) return rc;
+  if (int rc = need16(k_norm_w, "k_norm_w (latent norm weight)")) return rc;
+  if (int rc = need16(out, paged ? "k_pool" : "k")) return rc;
+  const int64_t row_bytes = L->in_row_stride * 2;
+  if (int rc = check_disjoint({{out, out_bytes}}, {{qkv, L->T * row_bytes}, {positions, L->T * 4}, {k_norm_w, 1024}}))
+    return rc;
+  int cus = 0;
+  if (int rc = current_device(&cus)) return rc;
+  LatentArgs a{};
+  a.rows = static_cast<const uint8_t*>(qkv);
+  a.row_bytes = row_bytes;
+  a.pos = positions;
+  a.w = static_cast<const uint8_t*>(k_norm_w);
+  a.out = static_cast<uint8_t*>(out);
+  a.eps = eps;
+  a.log2_theta = std::log2(theta);
+  a.T = L->T;
+  a.bt = bt;
+  a.bt_stride = bt_stride;
+  a.tokens_per_req = tokens_per_req;
+  a.page_size = page_size;
+  a.num_pages = num_pages;
+  int64_t grid = (L->T + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (grid > static_cast<int64_t>(cus) * kFwdBlocksPerCu) grid = static_cast<int64_t>(cus) * kFwdBlocksPerCu;
+  if (paged)
+    hipLaunchKernelGGL((fwd_latent_kernel<true>), dim3(grid), dim3(kBlockThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((fwd_latent_kernel<false>), dim3(grid), dim3(kBlockThreads), 0, stream, a);
+  return launched("latent forward");
+}
+
+int gqa_forward(const qkvnr_layout* L, const void* qkv, const int32_t* positions, const void* q_norm_w,
+                const void* k_norm_w, float eps, double theta, void* q, void* k, void* v, int64_t kv_bytes,
+                const int32_t* bt, int32_t bt_stride, int32_t tokens_per_req, int32_t page_size,
+                int32_t num_pages, bool paged, hipStream_t stream) {
+  const bool rope = L->rope_dim > 0;
+  const int es = elem_bytes(L->dtype);
+  if (L->T == 0) return QKVNR_OK;  // nothing is read or written
+  if (int rc = need16(qkv, "qkv")) return rc;
+  if (rope || paged) {
+    if (int rc = need4(positions, "positions")) return rc;
+  }
+  if (int rc = need16(q_norm_w, "q_norm_w")) return rc;
+  if (int rc = need16(k_norm_w, "k_norm_w")) return rc;
+  if (int rc = need16(q, "q")) return rc;
+  if (int rc = need16(k, paged ? "k_pool" : "k")) return rc;
+  if (int rc = need16(v, paged ? "v_pool" : "v")) return rc;
+  const int64_t D = L->head_dim, n_q = static_cast<int64_t>(L->n_kv) * L->q_per_kv;
+  const int64_t wbytes = D * es;
+  if (int rc = check_disjoint({{q, L->T * n_q * D * es}, {k, kv_bytes}, {v, kv_bytes}},
+                              {{qkv, L->T * L->in_row_stride * es},
+                               {positions, positions ? L->T * 4 : 0},
+                               {q_norm_w, wbytes},
+                               {k_norm_w, wbytes}}))
+    return rc;
+  int cus = 0;
+  if (int rc = current_device(&cus)) return rc;
+  GqaArgs a{};
+  const int grid = plan_gqa(a, L, cus, kFwdBlocksPerCu);
+  a.qkv = static_cast<const uint8_t*>(qkv);
+  a.pos = positions;
+  a.wq = static_cast<const uint8_t*>(q_norm_w);
+  a.wk = static_cast<const uint8_t*>(k_norm_w);
+  a.q = static_cast<uint8_t*>(q);
+  a.k = static_cast<uint8_t*>(k);
+  a.v = static_cast<uint8_t*>(v);
+  a.eps = eps;
+  a.log2_theta = rope ? std::log2(theta) : 0.0;
+  a.bt = bt;
+  a.bt_stride = bt_stride;
+  a.tokens_per_req = tokens_per_req;
+  a.page_size = page_size;
+  a.num_pages = num_pages;
+  if (paged)
+    launch_fwd_gqa<true>(a, L->dtype, L->head_dim, rope, grid, stream);
+  else
+    launch_fwd_gqa<false>(a, L->dtype, L->head_dim, rope, grid, stream);
+  return launched("forward");
+}
+
+}  // namespace
+
+extern "C" {
+
+int qkvnr_forward(const qkvnr_layout* layout, const void* qkv, const int32_t* positions, const void* q_norm_w,
+                  const void* k_norm_w, float eps, double theta, void* q, void* k, void* v, hipStream_t stream) {
+  if (int rc = check_layout(layout)) return rc;
+  if (int rc = check_scalars(layout, eps, theta)) return rc;
+  const qkvnr_layout* L = layout;
+  if (L->kind == QKVNR_LATENT) {
+    if (int rc = must_be_null(q_norm_w, "q_norm_w")) return rc;
+    if (int rc = must_be_null(q, "q")) return rc;
+    if (int rc = must_be_null(v, "v")) return rc;
+    return latent_forward(L, qkv, positions, k_norm_w, eps, theta, k, L->T * L->width * 2, nullptr, 0, 1, 1, 1,
+                          false, stream);
+  }
+  const int64_t kv_bytes = L->T * L->n_kv * static_cast<int64_t>(L->head_dim) * elem_bytes(L->dtype);
+  return gqa_forward(L, qkv, positions, q_norm_w, k_norm_w, eps, theta, q, k, v, kv_bytes, nullptr, 0, 1, 1, 1,
+                     false, stream);
+}
+
+int qkvnr_forward_paged(const qkvnr_layout* layout, const void* qkv, const int32_t* positions,
+                        const void* q_norm_w, const void* k_norm_w, float eps, double theta,
+                        const int32_t* block_table, int32_t bt_stride, int32_t tokens_per_req, int32_t page_size,
+                        int32_t num_pages, void* q, void* k_pool, void* v_pool, hipStream_t stream) {
+  if (int rc = check_layout(layout)) return rc;
+  if (int rc = check_scalars(layout, eps, theta)) return rc;
+  if (int rc = check_paged(block_table, bt_stride, tokens_per_req, page_size, num_pages)) return rc;
+  const qkvnr_layout* L = layout;
+  const int64_t slots = static_cast<int64_t>(num_pages) * page_size;
+  if (L->kind == QKVNR_LATENT) {
+    if (int rc = must_be_null(q_norm_w, "q_norm_w")) return rc;
+    if (int rc = must_be_null(q, "q")) return rc;
+    if (int rc = must_be_null(v_pool, "v_pool")) return rc;
+    return latent_forward(L, qkv, positions, k_norm_w, eps, theta, k_pool, slots * L->width * 2, block_table,
+                          bt_stride, tokens_per_req, page_size, num_pages, true, stream);
+  }
+  const int64_t kv_bytes = slots * L->n_kv * static_cast<int64_t>(L->head_dim) * elem_bytes(L->dtype);
+  return gqa_forward(L, qkv, positions, q_norm_w, k_norm_w, eps, theta, q, k_pool, v_pool, kv_bytes, block_table,
+                     bt_stride, tokens_per_req, page_size, num_pages, true, stream);
+}
+
+int qkvnr_backward(const qkvnr_layout* layout, const void* qkv, const int32_t* positions, const void* q_norm_w,
+                   const void* k_norm_w, float eps, double theta, const void* dq, const void* dk, const void* dv,
+                   void* dqkv, float* dq_norm_w, float* dk_norm_w, hipStream_t stream) {
+  if (int rc = check_layout(layout)) return rc;
+  const qkvnr_layout* L = layout;
+  if (L->kind == QKVNR_LATENT) return fail(QKVNR_EUNSUPPORTED, "backward of latent rows has no kernel");
+  if (int rc = check_scalars(L, eps, theta)) return rc;
+  const bool rope = L->rope_dim > 0;
+  const int es = elem_bytes(L->dtype);
+  if (int rc = need4(dq_norm_w, "dq_norm_w")) return rc;
+  if (int rc = need4(dk_norm_w, "dk_norm_w")) return rc;
+  const int64_t D = L->head_dim, n_q = static_cast<int64_t>(L->n_kv) * L->q_per_kv;
+  if (overlaps({dq_norm_w, D * 4}, {dk_norm_w, D * 4})) return fail(QKVNR_EINVAL, "two outputs overlap");
+  int cus = 0;
+  if (L->T == 0) {  // no token is read: only the weight grads are written (zero)
+    if (int rc = current_device(&cus)) return rc;
+    hipLaunchKernelGGL(zero2_f32_kernel, dim3(1), dim3(256), 0, stream, dq_norm_w, dk_norm_w, static_cast<int>(D));
+    return launched("weight-grad zeroing");
+  }
+  if (int rc = need16(qkv, "qkv")) return rc;
+  if (rope) {
+    if (int rc = need4(positions, "positions")) return rc;
+  }
+  if (int rc = need16(q_norm_w, "q_norm_w")) return rc;
+  if (int rc = need16(k_norm_w, "k_norm_w")) return rc;
+  if (int rc = need16(dq, "dq")) return rc;
+  if (int rc = need16(dk, "dk")) return rc;
+  if (int rc = need16(dv, "dv")) return rc;
+  if (int rc = need16(dqkv, "dqkv")) return rc;
+  const int64_t kvb = L->T * L->n_kv * D * es;
+  if (int rc = check_disjoint(
+          {{dqkv, L->T * L->in_row_stride * es}, {dq_norm_w, D * 4}, {dk_norm_w, D * 4}},
+          {{qkv, L->T * L->in_row_stride * es}, {positions, positions ? L->T * 4 : 0}, {q_norm_w, D * es},
+           {k_norm_w, D * es}, {dq, L->T * n_q * D * es}, {dk, kvb}, {dv, kvb}}))
+    return rc;
+  if (int rc = current_device(&cus)) return rc;
+  hipLaunchKernelGGL(zero2_f32_kernel, dim3(1), dim3(256), 0, stream, dq_norm_w, dk_norm_w, static_cast<int>(D));
+  if (int rc = launched("weight-grad zeroing")) return rc;
+  GqaArgs a{};
+  const int grid = plan_gqa(a, L, cus, kBwdBlocksPerCu);
+  a.qkv = static_cast<const uint8_t*>(qkv);
+  a.pos = positions;
+  a.wq = static_cast<const uint8_t*>(q_norm_w);
+  a.wk = static_cast<const uint8_t*>(k_norm_w);
+  a.dq = static_cast<const uint8_t*>(dq);
+  a.dk = static_cast<const uint8_t*>(dk);
+  a.dv = static_cast<const uint8_t*>(dv);
+  a.dqkv = static_cast<uint8_t*>(dqkv);
+  a.dwq = dq_norm_w;
+  a.dwk = dk_norm_w;
+  a.eps = eps;
+  a.log2_theta = rope ? std::log2(theta) : 0.0;
+  launch_bwd_gqa(a, L->dtype, L->head_dim, rope, grid, stream);
+  return launched("backward");
+}
+
+const char* qkvnr_strerror(int code) {
+  switch (code) {
+    case QKVNR_OK:
+      return "ok";
+    case QKVNR_EINVAL:
+    case QKVNR_EALIGN:
+    case QKVNR_EUNSUPPORTED:
+    case QKVNR_EHIP:
+      return g_msg[0] ? g_msg : "error";
+    default:
+      return "unknown qkvnr return code";
+  }
+}
+
+int qkvnr_version(void) { return QKVNR_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,174 @@
+"""C-ABI library: loading, exported symbols and host-side validation (CPU only).
+
+Every call here is rejected by the host checks before the library makes any
+HIP call (or is a T = 0 forward, which enqueues nothing), so the fake device
+addresses below are never dereferenced and no kernel is ever launched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import qkv_split_head_amd as qk
+from qkv_split_head_amd import Layout
+
+A = 0x7F0000000000  # a 16-byte aligned fake device address, never dereferenced
+B = A + (1 << 30)
+C = A + (2 << 30)
+Dp = A + (3 << 30)
+E = A + (4 << 30)
+F = A + (5 << 30)
+
+
+def _lay(kind=qk.INTERLEAVED, dtype=qk.BF16, T=4, n_kv=16, q_per_kv=8, head_dim=64, rope_dim=64, width=None,
+         stride=None, norm_dim=0):
+    w = (n_kv * q_per_kv + 2 * n_kv) * head_dim if width is None else width
+    return Layout(kind=kind, dtype=dtype, T=T, n_kv=n_kv, q_per_kv=q_per_kv, head_dim=head_dim,
+                  rope_dim=rope_dim, norm_dim=norm_dim, reserved=0, width=w,
+                  in_row_stride=w if stride is None else stride)
+
+
+def _fwd(L, qkv=A, pos=B, wq=C, wk=C + 4096, q=Dp, k=E, v=F, eps=1e-6, theta=1e4):
+    return qk.lib().qkvnr_forward(ctypes.byref(L), qkv, pos, wq, wk, eps, theta, q, k, v, None)
+
+
+def test_library_exports_every_header_function():
+    lib = qk.lib()
+    names = qk.header_functions()
+    assert {"qkvnr_forward", "qkvnr_backward", "qkvnr_forward_paged", "qkvnr_strerror",
+            "qkvnr_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_matches_header():
+    text = open(os.path.join(os.path.dirname(qk.__file__), "..", "include", "qkvnr.h")).read()
+    v = int(re.search(r"#define QKVNR_VERSION (\d+)", text).group(1))
+    assert qk.qkvnr_version() == v
+
+
+def test_layout_struct_matches_c_size():
+    # int32 kind, dtype; int64 T; 6 x int32; int64 width, in_row_stride
+    assert ctypes.sizeof(Layout) == 56
+    assert Layout.width.offset == 40 and Layout.in_row_stride.offset == 48 and Layout.T.offset == 8
+
+
+def test_null_layout():
+    assert qk.lib().qkvnr_forward(None, A, B, C, C, 1e-6, 1e4, Dp, E, F, None) == qk.EINVAL
+
+
+@pytest.mark.parametrize("field,value", [("kind", 7), ("dtype", 5), ("T", -1), ("n_kv", 0), ("q_per_kv", 0)])
+def test_bad_descriptor_fields(field, value):
+    L = _lay()
+    setattr(L, field, value)
+    assert _fwd(L) == qk.EINVAL
+
+
+def test_exact_total_guard_declines_wrong_width():
+    # a descriptor claiming 8 kv heads for a row built with 1 (the multi-query case):
+    # (8 + 2*8) * 64 = 1536 described, (8 + 2*1) * 64 = 640 present
+    L = _lay(n_kv=8, q_per_kv=1, width=640)
+    assert _fwd(L) == qk.EINVAL
+    assert "exact total" in qk.lib().qkvnr_strerror(qk.EINVAL).decode()
+
+
+def test_unsupported_head_dim_and_partial_rope():
+    assert _fwd(_lay(head_dim=96, rope_dim=96)) == qk.EUNSUPPORTED
+    assert _fwd(_lay(head_dim=64, rope_dim=32)) == qk.EUNSUPPORTED
+    assert _fwd(_lay(head_dim=64, rope_dim=33)) == qk.EINVAL
+    assert _fwd(_lay(head_dim=64, rope_dim=128)) == qk.EINVAL
+
+
+def test_row_stride_checks():
+    w = (16 * 8 + 32) * 64
+    assert _fwd(_lay(stride=w - 8)) == qk.EINVAL
+    assert _fwd(_lay(stride=w + 1)) == qk.EALIGN  # 2 bytes past a 16-byte multiple
+
+
+def test_pointer_checks():
+    assert _fwd(_lay(), qkv=0) == qk.EINVAL
+    assert _fwd(_lay(), qkv=A + 8) == qk.EALIGN
+    assert _fwd(_lay(), pos=0) == qk.EINVAL          # RoPE layer needs positions
+    assert _fwd(_lay(), pos=B + 2) == qk.EALIGN
+    assert _fwd(_lay(), q=0) == qk.EINVAL
+    assert _fwd(_lay(), wk=C + 8) == qk.EALIGN
+
+
+def test_scalar_checks():
+    assert _fwd(_lay(), eps=-1.0) == qk.EINVAL
+    assert _fwd(_lay(), eps=float("nan")) == qk.EINVAL
+    assert _fwd(_lay(), theta=0.0) == qk.EINVAL
+    assert _fwd(_lay(), theta=float("inf")) == qk.EINVAL
+
+
+def test_outputs_must_not_overlap_inputs():
+    assert _fwd(_lay(), q=A + 1024) == qk.EINVAL  # q inside qkv
+    assert _fwd(_lay(), k=Dp + 16) == qk.EINVAL   # k inside q
+
+
+def test_empty_batch_forward_enqueues_nothing():
+    # T = 0 passes validation and returns before any HIP call
+    assert _fwd(_lay(T=0)) == qk.OK
+    # NoPE layers do not need positions
+    assert _fwd(_lay(T=0, rope_dim=0), pos=0) == qk.OK
+
+
+def test_latent_descriptor_checks():
+    lat = _lay(kind=qk.LATENT, n_kv=1, q_per_kv=0, head_dim=0, rope_dim=64, norm_dim=512, width=576)
+    assert qk.lib().qkvnr_forward(ctypes.byref(lat), A, B, C, C, 1e-6, 1e4, None, Dp, None, None) == qk.EINVAL
+    assert qk.lib().qkvnr_forward(ctypes.byref(lat), A, B, None, C, 1e-6, 1e4, Dp, Dp, None, None) == qk.EINVAL
+    bad_w = _lay(kind=qk.LATENT, n_kv=1, q_per_kv=0, head_dim=0, rope_dim=64, norm_dim=512, width=512)
+    assert qk.lib().qkvnr_forward(ctypes.byref(bad_w), A, B, None, C, 1e-6, 1e4, None, Dp, None, None) == qk.EINVAL
+    f32 = _lay(kind=qk.LATENT, dtype=qk.FP32, n_kv=1, q_per_kv=0, head_dim=0, rope_dim=64, norm_dim=512, width=576)
+    assert qk.lib().qkvnr_forward(ctypes.byref(f32), A, B, None, C, 1e-6, 1e4, None, Dp, None, None) == qk.EUNSUPPORTED
+    n256 = _lay(kind=qk.LATENT, n_kv=1, q_per_kv=0, head_dim=0, rope_dim=64, norm_dim=256, width=320)
+    assert qk.lib().qkvnr_forward(ctypes.byref(n256), A, B, None, C, 1e-6, 1e4, None, Dp, None, None) == qk.EUNSUPPORTED
+    assert qk.lib().qkvnr_backward(ctypes.byref(lat), A, B, None, C, 1e-6, 1e4, A, A, A, Dp, E, F, None) == qk.EUNSUPPORTED
+
+
+def test_latent_empty_batch():
+    lat = _lay(kind=qk.LATENT, T=0, n_kv=1, q_per_kv=0, head_dim=0, rope_dim=64, norm_dim=512, width=576)
+    assert qk.lib().qkvnr_forward(ctypes.byref(lat), A, B, None, C, 1e-6, 1e4, None, Dp, None, None) == qk.OK
+
+
+def test_paged_argument_checks():
+    L = _lay()
+    f = qk.lib().qkvnr_forward_paged
+    assert f(ctypes.byref(L), A, B, C, C + 4096, 1e-6, 1e4, None, 4, 4, 64, 16, Dp, E, F, None) == qk.EINVAL
+    assert f(ctypes.byref(L), A, B, C, C + 4096, 1e-6, 1e4, A + (6 << 30), 4, 4, 0, 16, Dp, E, F, None) == qk.EINVAL
+    assert f(ctypes.byref(L), A, B, C, C + 4096, 1e-6, 1e4, A + (6 << 30) + 2, 4, 4, 64, 16, Dp, E, F,
+             None) == qk.EALIGN
+    L0 = _lay(T=0)
+    assert f(ctypes.byref(L0), A, B, C, C + 4096, 1e-6, 1e4, A + (6 << 30), 4, 4, 64, 16, Dp, E, F, None) == qk.OK
+
+
+def test_backward_argument_checks():
+    L = _lay()
+    f = qk.lib().qkvnr_backward
+    args = [A, B, C, C + 4096, 1e-6, 1e4, Dp, E, F, A + (6 << 30), A + (7 << 30), A + (7 << 30) + 4096]
+    a = list(args)
+    a[9] = 0  # dqkv NULL
+    assert f(ctypes.byref(L), *a, None) == qk.EINVAL
+    a = list(args)
+    a[10] = A + (7 << 30) + 2  # dq_norm_w misaligned
+    assert f(ctypes.byref(L), *a, None) == qk.EALIGN
+    a = list(args)
+    a[9] = A + 64  # dqkv overlaps qkv
+    assert f(ctypes.byref(L), *a, None) == qk.EINVAL
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU driver is present; this case is for GPU-less hosts")
+def test_valid_call_without_gpu_is_unsupported_not_a_crash():
+    # every argument valid: the library reaches its device query, finds no gfx950, and says so
+    assert _fwd(_lay()) == qk.EUNSUPPORTED
+    assert "gfx950" in qk.lib().qkvnr_strerror(qk.EUNSUPPORTED).decode() or \
+        "device" in qk.lib().qkvnr_strerror(qk.EUNSUPPORTED).decode()
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    import qkv_split_head_amd._binding as b
+    monkeypatch.setattr(b, "_lib", None)
+    monkeypatch.setattr(b, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="no fallback"):
+        b.lib()

@@ -1,0 +1,473 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 CPU oracle.
+
+Rules (see tests/helpers.py): bf16 within 2 bf16 ulps with an rms floor, fp32
+within 1e-5 relative, v / dv / store locations / untouched memory bit-exact.
+Inputs are the seeded generators of ``qkv_inputs``; the oracle and the library
+see the same bits.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import qkv_split_head_amd as qk
+from qkv_inputs import (custom_gqa, decode_interleaved, gqa_paged, latent_paged, prefill_interleaved,
+                        tiny_interleaved, train_sectioned)
+from tests.helpers import (announce, assert_bits_equal, assert_close, assert_values_close, gpu_available,
+                           host_value, to_dev, to_host_bits)
+
+pytestmark = pytest.mark.gpu
+
+SENT16 = 0x7FC1  # a NaN pattern no kernel result can equal
+SENT32 = 0x7FC00001
+
+
+@pytest.fixture(autouse=True)
+def _gpu(request):
+    if not gpu_available():
+        pytest.skip("no GPU")
+    qk.lib()  # fails loudly when the library is missing
+    announce(request.node.nodeid)
+    yield
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ helpers
+
+
+def _sentinel_buffer(n_elems: int, dtype: str, pad: int):
+    """Device buffer of n_elems + 2*pad elements filled with a NaN sentinel; returns (buf, middle view)."""
+    if dtype == "bf16":
+        buf = torch.full((n_elems + 2 * pad,), SENT16, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    else:
+        buf = torch.full((n_elems + 2 * pad,), SENT32, dtype=torch.int32, device="cuda").view(torch.float32)
+    return buf, buf[pad:pad + n_elems]
+
+
+def _pads_untouched(buf: torch.Tensor, pad: int, what: str):
+    raw = buf.view(torch.int16) if buf.dtype == torch.bfloat16 else buf.view(torch.int32)
+    sent = SENT16 if buf.dtype == torch.bfloat16 else SENT32
+    assert bool((raw[:pad] == sent).all()) and bool((raw[raw.numel() - pad:] == sent).all()), \
+        f"{what}: guard band overwritten"
+
+
+def _dev_inputs(w):
+    return (to_dev(w.qkv, w.dtype), to_dev(w.positions, "int32"), to_dev(w.q_norm_w, w.dtype),
+            to_dev(w.k_norm_w, w.dtype))
+
+
+def _gpu_forward(w, pad=64, stream=None):
+    """Run the forward into guard-banded outputs; returns host bits of q, k, v."""
+    qkv, pos, wq, wk = _dev_inputs(w)
+    T, D = w.T, w.head_dim
+    bq, q = _sentinel_buffer(T * w.n_q * D, w.dtype, pad)
+    bk, k = _sentinel_buffer(T * w.n_kv * D, w.dtype, pad)
+    bv, v = _sentinel_buffer(T * w.n_kv * D, w.dtype, pad)
+    out = (q.view(T, w.n_q, D), k.view(T, w.n_kv, D), v.view(T, w.n_kv, D))
+    qk.forward(qkv, pos, wq, wk, kind=w.kind, n_kv=w.n_kv, q_per_kv=w.q_per_kv, head_dim=D,
+               rope=w.rope_dim > 0, eps=w.eps, theta=w.theta, out=out, stream=stream)
+    torch.cuda.synchronize()
+    for b, n in [(bq, "q"), (bk, "k"), (bv, "v")]:
+        _pads_untouched(b, pad, n)
+    return tuple(to_host_bits(t) for t in out)
+
+
+def _check_forward(w, got, tokens=None):
+    sel = slice(None) if tokens is None else tokens
+    q64, k64, vbits = oracle.forward_gqa(w.qkv[sel], w.dtype, w.kind, w.n_kv, w.q_per_kv, w.head_dim,
+                                         w.positions[sel], w.q_norm_w, w.k_norm_w, w.eps, w.theta,
+                                         rope=w.rope_dim > 0)
+    gq, gk, gv = (g[sel] for g in got)
+    assert_close(gq, q64, w.dtype, f"{w.name} q")
+    assert_close(gk, k64, w.dtype, f"{w.name} k")
+    assert_bits_equal(gv, vbits, f"{w.name} v")
+
+
+def _gpu_backward(w, stream=None):
+    qkv, pos, wq, wk = _dev_inputs(w)
+    dq, dk, dv = to_dev(w.dq, w.dtype), to_dev(w.dk, w.dtype), to_dev(w.dv, w.dtype)
+    dqkv, dwq, dwk = qk.backward(qkv, pos, wq, wk, dq, dk, dv, kind=w.kind, n_kv=w.n_kv, q_per_kv=w.q_per_kv,
+                                 head_dim=w.head_dim, rope=w.rope_dim > 0, eps=w.eps, theta=w.theta,
+                                 stream=stream)
+    torch.cuda.synchronize()
+    return to_host_bits(dqkv), dwq.cpu().numpy().astype(np.float64), dwk.cpu().numpy().astype(np.float64)
+
+
+def _check_backward(w, dqkv_bits, dwq, dwk, tokens=None, ref=None):
+    sel = slice(None) if tokens is None else tokens
+    if ref is None:
+        ref = oracle.backward_gqa(w.qkv, w.dtype, w.kind, w.n_kv, w.q_per_kv, w.head_dim, w.positions,
+                                  w.q_norm_w, w.k_norm_w, w.eps, w.theta, w.dq, w.dk, w.dv,
+                                  rope=w.rope_dim > 0)
+    gq, gk, gv = oracle.split(dqkv_bits[sel], w.kind, w.n_kv, w.q_per_kv, w.head_dim)
+    assert_close(gq, ref["dx_q"][sel], w.dtype, f"{w.name} dq slots")
+    assert_close(gk, ref["dx_k"][sel], w.dtype, f"{w.name} dk slots")
+    assert_bits_equal(gv, w.dv[sel], f"{w.name} dv slots")
+    assert_values_close(dwq, ref["dw_q"], w.dtype, f"{w.name} dq_norm_w", scale=ref["dw_q_l2"])
+    assert_values_close(dwk, ref["dw_k"], w.dtype, f"{w.name} dk_norm_w", scale=ref["dw_k_l2"])
+
+
+def _sample_tokens(T, n=64, seed=0):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    mid = rng.choice(np.arange(3, T - 3), size=min(n - 6, T - 6), replace=False)
+    return np.unique(np.concatenate([np.arange(3), mid, np.arange(T - 3, T)]))
+
+
+# ------------------------------------------------------------------ named workloads (small)
+
+
+def test_tiny_fp32_interleaved():
+    w = tiny_interleaved()
+    _check_forward(w, _gpu_forward(w))
+
+
+@pytest.mark.parametrize("T", [1, 8, 64, 256])
+def test_muse_decode(T):
+    w = decode_interleaved(T)
+    _check_forward(w, _gpu_forward(w))
+
+
+# ------------------------------------------------------------------ forward, shapes and edge cases
+
+FWD_CASES = [
+    # kind, dtype, T, n_kv, q_per_kv, D, rope, positions
+    ("interleaved", "bf16", 300, 16, 8, 64, True, "random"),
+    ("interleaved", "bf16", 777, 3, 5, 64, True, "random"),    # 21 heads: ragged last iteration
+    ("interleaved", "bf16", 129, 2, 3, 128, True, "random"),
+    ("interleaved", "fp32", 95, 2, 4, 64, True, "random"),
+    ("interleaved", "fp32", 70, 3, 2, 128, True, "random"),    # 32 lanes per head
+    ("sectioned", "bf16", 257, 8, 4, 128, True, "arange"),
+    ("sectioned", "bf16", 333, 1, 1, 64, True, "random"),      # 3 heads per token
+    ("sectioned", "fp32", 64, 2, 7, 128, True, "random"),
+    ("sectioned", "bf16", 100, 4, 2, 64, False, "random"),     # NoPE
+    ("interleaved", "fp32", 50, 2, 2, 64, False, "random"),    # NoPE fp32
+    ("interleaved", "bf16", 5000, 4, 4, 64, True, "arange"),   # many units per wave
+]
+
+
+@pytest.mark.parametrize("case", FWD_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_forward_shapes(case):
+    kind, dtype, T, n_kv, Q, D, rope, posmode = case
+    w = custom_gqa(kind, dtype, T, n_kv, Q, D, rope=rope, theta=5e5, seed=T + D, positions=posmode)
+    _check_forward(w, _gpu_forward(w))
+
+
+def test_forward_positions_near_int32_max():
+    w = custom_gqa("interleaved", "fp32", 40, 2, 2, 64, theta=1e4, seed=9, positions="random",
+                   max_pos=2 ** 31 - 1)
+    w.positions[:4] = [2 ** 31 - 1, 2 ** 31 - 2, 2 ** 30, 0]
+    _check_forward(w, _gpu_forward(w))
+
+
+def test_forward_zero_heads_stay_zero():
+    w = custom_gqa("interleaved", "bf16", 9, 2, 2, 64, seed=3, positions="random")
+    w.qkv[2] = 0  # a token whose every head is zero: normed and rotated value is 0 with eps > 0
+    got = _gpu_forward(w)
+    _check_forward(w, got)
+    assert (host_value(got[0][2], "bf16") == 0).all() and (host_value(got[1][2], "bf16") == 0).all()
+
+
+def test_forward_padded_row_stride():
+    w = custom_gqa("sectioned", "bf16", 123, 2, 3, 128, seed=4, positions="random")
+    width = w.width
+    big = np.full((w.T, width + 24), SENT16, dtype=np.uint16)  # 48 extra bytes per row
+    big[:, :width] = w.qkv
+    qkv = to_dev(big, "bf16")[:, :width]
+    pos = to_dev(w.positions, "int32")
+    q, k, v = qk.forward(qkv, pos, to_dev(w.q_norm_w, "bf16"), to_dev(w.k_norm_w, "bf16"), kind="sectioned",
+                         n_kv=2, q_per_kv=3, head_dim=128, eps=w.eps, theta=w.theta)
+    torch.cuda.synchronize()
+    _check_forward(w, (to_host_bits(q), to_host_bits(k), to_host_bits(v)))
+
+
+def test_forward_empty_batch():
+    w = custom_gqa("interleaved", "bf16", 0, 2, 2, 64, seed=1)
+    q, k, v = qk.forward(to_dev(w.qkv, "bf16"), to_dev(w.positions, "int32"), to_dev(w.q_norm_w, "bf16"),
+                         to_dev(w.k_norm_w, "bf16"), kind="interleaved", n_kv=2, q_per_kv=2, head_dim=64)
+    torch.cuda.synchronize()
+    assert q.shape == (0, 4, 64) and k.shape == (0, 2, 64)
+
+
+def test_forward_rejects_misaligned_device_pointer():
+    w = custom_gqa("interleaved", "bf16", 4, 2, 2, 64, seed=1)
+    big = to_dev(np.concatenate([np.zeros(1, np.uint16), w.qkv.reshape(-1)]), "bf16")
+    qkv = big[1:].view(4, 2, 4, 64)  # 2 bytes off a 16-byte boundary
+    with pytest.raises(qk.QkvnrError) as ei:
+        qk.forward(qkv, to_dev(w.positions, "int32"), to_dev(w.q_norm_w, "bf16"), to_dev(w.k_norm_w, "bf16"),
+                   kind="interleaved", n_kv=2, q_per_kv=2, head_dim=64)
+    assert ei.value.code == qk.EALIGN
+
+
+# ------------------------------------------------------------------ GPU-vs-GPU bitwise equivalences
+
+
+def test_nope_layer_equals_rope_at_position_zero_bitwise():
+    w = custom_gqa("interleaved", "bf16", 200, 16, 8, 64, seed=5, positions="random")
+    w.rope_dim = 0
+    nope = _gpu_forward(w)
+    w.rope_dim = 64
+    w.positions = np.zeros_like(w.positions)
+    rope0 = _gpu_forward(w)
+    for a, b, n in zip(nope, rope0, "qkv"):
+        assert_bits_equal(a, b, f"NoPE vs RoPE@0 {n}")
+
+
+def _interleaved_to_sectioned_blocks(n_kv, Q):
+    n_q = n_kv * Q
+    return np.array([g * Q + s if s < Q else (n_q + g if s == Q else n_q + n_kv + g)
+                     for g in range(n_kv) for s in range(Q + 2)])
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("bf16", 128), ("fp32", 64)])
+def test_layouts_give_the_same_heads_bitwise(dtype, D):
+    T, n_kv, Q = 150, 4, 3
+    wi = custom_gqa("interleaved", dtype, T, n_kv, Q, D, seed=6, positions="random", grads=True)
+    perm = _interleaved_to_sectioned_blocks(n_kv, Q)
+    H = n_kv * (Q + 2)
+    xs = np.empty_like(wi.qkv.reshape(T, H, D))
+    xs[:, perm] = wi.qkv.reshape(T, H, D)
+    ws = custom_gqa("sectioned", dtype, T, n_kv, Q, D, seed=6, positions="random", grads=True)
+    ws.qkv = xs.reshape(T, H * D)
+    ws.q_norm_w, ws.k_norm_w, ws.positions = wi.q_norm_w, wi.k_norm_w, wi.positions
+    ws.dq, ws.dk, ws.dv = wi.dq, wi.dk, wi.dv
+    for a, b, n in zip(_gpu_forward(wi), _gpu_forward(ws), "qkv"):
+        assert_bits_equal(a, b, f"interleaved vs sectioned {n}")
+    di, dwqi, dwki = _gpu_backward(wi)
+    ds, dwqs, dwks = _gpu_backward(ws)
+    assert_bits_equal(di.reshape(T, H, D), ds.reshape(T, H, D)[:, perm], "dqkv block permutation")
+    # weight grads are summed with atomics: same values up to summation order
+    assert np.allclose(dwqi, dwqs, rtol=1e-5, atol=1e-5 * np.abs(dwqi).max())
+    assert np.allclose(dwki, dwks, rtol=1e-5, atol=1e-5 * np.abs(dwki).max())
+
+
+def test_forward_is_deterministic_and_honours_the_stream():
+    w = custom_gqa("interleaved", "bf16", 1000, 16, 8, 64, seed=7, positions="random")
+    a = _gpu_forward(w)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        b = _gpu_forward(w, stream=s)
+    for x, y, n in zip(a, b, "qkv"):
+        assert_bits_equal(x, y, f"rerun {n}")
+
+
+# ------------------------------------------------------------------ backward
+
+BWD_CASES = [
+    ("interleaved", "bf16", 300, 16, 8, 64, True),
+    ("interleaved", "bf16", 211, 3, 5, 64, True),
+    ("sectioned", "bf16", 257, 8, 4, 128, True),
+    ("sectioned", "bf16", 97, 2, 3, 128, False),
+    ("interleaved", "fp32", 80, 2, 4, 64, True),
+    ("sectioned", "fp32", 66, 3, 2, 128, True),
+    ("interleaved", "fp32", 40, 1, 1, 64, False),
+    ("interleaved", "bf16", 3000, 4, 4, 128, True),
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_backward_shapes(case):
+    kind, dtype, T, n_kv, Q, D, rope = case
+    w = custom_gqa(kind, dtype, T, n_kv, Q, D, rope=rope, theta=1e6, seed=T * 3 + D, positions="random",
+                   grads=True)
+    _check_backward(w, *_gpu_backward(w))
+
+
+def test_backward_padded_row_stride_leaves_padding():
+    w = custom_gqa("interleaved", "bf16", 77, 2, 4, 64, seed=8, positions="random", grads=True)
+    width = w.width
+    big = np.full((w.T, width + 8), SENT16, dtype=np.uint16)
+    big[:, :width] = w.qkv.reshape(w.T, width)
+    qkv = to_dev(big, "bf16")[:, :width]
+    dqkv_big = torch.full((w.T, width + 8), SENT16, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    dqkv = dqkv_big[:, :width]
+    dwq = torch.full((64,), float("nan"), device="cuda")
+    dwk = torch.full((64,), float("nan"), device="cuda")
+    qk.backward(qkv, to_dev(w.positions, "int32"), to_dev(w.q_norm_w, "bf16"), to_dev(w.k_norm_w, "bf16"),
+                to_dev(w.dq, "bf16"), to_dev(w.dk, "bf16"), to_dev(w.dv, "bf16"), kind="interleaved", n_kv=2,
+                q_per_kv=4, head_dim=64, eps=w.eps, theta=w.theta, out=(dqkv, dwq, dwk))
+    torch.cuda.synchronize()
+    pad = to_host_bits(dqkv_big)[:, width:]
+    assert (pad == SENT16).all()
+    got = to_host_bits(dqkv_big)[:, :width].reshape(w.qkv.shape)
+    _check_backward(w, got, dwq.cpu().numpy().astype(np.float64), dwk.cpu().numpy().astype(np.float64))
+
+
+def test_backward_empty_batch_zeroes_weight_grads():
+    w = custom_gqa("sectioned", "bf16", 0, 2, 2, 128, seed=1, grads=True)
+    dwq = torch.full((128,), float("nan"), device="cuda")
+    dwk = torch.full((128,), float("nan"), device="cuda")
+    dqkv = torch.empty((0, w.width), dtype=torch.bfloat16, device="cuda")
+    qk.backward(to_dev(w.qkv, "bf16"), to_dev(w.positions, "int32"), to_dev(w.q_norm_w, "bf16"),
+                to_dev(w.k_norm_w, "bf16"), to_dev(w.dq, "bf16"), to_dev(w.dk, "bf16"), to_dev(w.dv, "bf16"),
+                kind="sectioned", n_kv=2, q_per_kv=2, head_dim=128, out=(dqkv, dwq, dwk))
+    torch.cuda.synchronize()
+    assert bool((dwq == 0).all()) and bool((dwk == 0).all())
+
+
+def test_backward_weight_grads_are_overwritten_not_accumulated():
+    w = custom_gqa("interleaved", "bf16", 64, 2, 2, 64, seed=10, positions="random", grads=True)
+    a = _gpu_backward(w)
+    b = _gpu_backward(w)
+    assert np.allclose(a[1], b[1], rtol=1e-5) and np.allclose(a[2], b[2], rtol=1e-5)
+    assert_bits_equal(a[0], b[0], "dqkv rerun")
+
+
+# ------------------------------------------------------------------ paged store
+
+
+@pytest.mark.parametrize("kind,dtype,D", [("interleaved", "bf16", 64), ("sectioned", "bf16", 128),
+                                          ("interleaved", "fp32", 64)])
+def test_gqa_paged_direct_equals_staged_scatter(kind, dtype, D):
+    w = gqa_paged(kind, dtype, B=3, T_req=7, n_kv=2, q_per_kv=4, head_dim=D, num_pages=300, page_size=16,
+                  ctx_hi=1500, seed=11)
+    qkv, pos, wq, wk = _dev_inputs(w)
+    shape = (w.num_pages, w.page_size, w.n_kv, D)
+    pools = [_sentinel_buffer(int(np.prod(shape)), dtype, 0)[1].view(shape) for _ in range(4)]
+    kp, vp, ks, vs = pools
+    bt = to_dev(w.block_table, "int32")
+    q_direct = qk.forward_paged(qkv, pos, wq, wk, bt, kp, vp, kind=kind, n_kv=2, q_per_kv=4, head_dim=D,
+                                tokens_per_req=w.tokens_per_req, eps=w.eps, theta=w.theta)
+    q_c, k_c, v_c = qk.forward(qkv, pos, wq, wk, kind=kind, n_kv=2, q_per_kv=4, head_dim=D, eps=w.eps,
+                               theta=w.theta)
+    page, off = oracle.paged_slots(w.positions, w.block_table, w.tokens_per_req, w.page_size)
+    slot = torch.from_numpy(page * w.page_size + off).cuda()
+    ks.view(-1, w.n_kv, D)[slot] = k_c
+    vs.view(-1, w.n_kv, D)[slot] = v_c
+    torch.cuda.synchronize()
+    assert_bits_equal(to_host_bits(q_direct), to_host_bits(q_c), "paged q")
+    assert_bits_equal(to_host_bits(kp), to_host_bits(ks), "k pool direct vs staged")
+    assert_bits_equal(to_host_bits(vp), to_host_bits(vs), "v pool direct vs staged")
+    # written rows against the oracle, and every other row untouched
+    kh = to_host_bits(kp)
+    written = np.zeros(shape[:2], dtype=bool)
+    written[page, off] = True
+    q64, k64, vbits = oracle.forward_gqa(w.qkv, dtype, kind, 2, 4, D, w.positions, w.q_norm_w, w.k_norm_w,
+                                         w.eps, w.theta)
+    assert_close(kh[page, off], k64, dtype, "paged k rows")
+    assert_bits_equal(to_host_bits(vp)[page, off], vbits, "paged v rows")
+    rest = kh[~written]
+    if dtype == "bf16":
+        assert (rest.view(np.uint16) == SENT16).all()
+    else:
+        assert (rest.view(np.uint32) == SENT32).all()
+
+
+def test_gqa_paged_skips_unmapped_tokens():
+    w = gqa_paged("interleaved", "bf16", B=2, T_req=4, n_kv=1, q_per_kv=2, head_dim=64, num_pages=64,
+                  page_size=16, ctx_hi=300, seed=12)
+    page, off = oracle.paged_slots(w.positions, w.block_table, w.tokens_per_req, w.page_size)
+    bad_tbl = w.block_table.copy()
+    bad_tbl[1, :] = -1  # request 1 unmapped
+    qkv, pos, wq, wk = _dev_inputs(w)
+    shape = (w.num_pages, w.page_size, 1, 64)
+    kp = _sentinel_buffer(int(np.prod(shape)), "bf16", 0)[1].view(shape)
+    vp = _sentinel_buffer(int(np.prod(shape)), "bf16", 0)[1].view(shape)
+    qk.forward_paged(qkv, pos, wq, wk, to_dev(bad_tbl, "int32"), kp, vp, kind="interleaved", n_kv=1,
+                     q_per_kv=2, head_dim=64, tokens_per_req=4, eps=w.eps, theta=w.theta)
+    torch.cuda.synchronize()
+    kh = to_host_bits(kp)
+    assert (kh[page[4:], off[4:]] == SENT16).all()  # request 1 not stored
+    assert not (kh[page[:4], off[:4]] == SENT16).any()  # request 0 stored
+
+
+def test_latent_rows_contiguous():
+    w = latent_paged(B=8, T_req=37, num_pages=32768, ctx_lo=0, ctx_hi=131072, seed=13)
+    rows = to_dev(w.qkv, "bf16")
+    out = qk.forward_latent(rows, to_dev(w.positions, "int32"), to_dev(w.k_norm_w, "bf16"), eps=w.eps,
+                            theta=w.theta)
+    torch.cuda.synchronize()
+    ref = oracle.latent_forward(w.qkv, "bf16", w.positions, w.k_norm_w, w.eps, w.theta, 512, 64)
+    got = to_host_bits(out)
+    assert_close(got[:, :512], ref[:, :512], "bf16", "latent normed part")
+    assert_close(got[:, 512:], ref[:, 512:], "bf16", "latent rotated part")
+
+
+def test_mla_latent_paged_store_full_pool():
+    # B = 4 requests x 16 draft tokens into a [8192, 64, 576] bf16 pool
+    w = latent_paged()
+    rows, pos, wk = to_dev(w.qkv, "bf16"), to_dev(w.positions, "int32"), to_dev(w.k_norm_w, "bf16")
+    shape = (w.num_pages, w.page_size, 576)
+    pool = _sentinel_buffer(int(np.prod(shape)), "bf16", 0)[1].view(shape)
+    qk.forward_latent_paged(rows, pos, wk, to_dev(w.block_table, "int32"), pool,
+                            tokens_per_req=w.tokens_per_req, eps=w.eps, theta=w.theta)
+    staged = qk.forward_latent(rows, pos, wk, eps=w.eps, theta=w.theta)
+    page, off = oracle.paged_slots(w.positions, w.block_table, w.tokens_per_req, w.page_size)
+    pt, ot = torch.from_numpy(page).cuda(), torch.from_numpy(off).cuda()
+    torch.cuda.synchronize()
+    assert_bits_equal(to_host_bits(pool[pt, ot]), to_host_bits(staged), "latent pool rows vs staged")
+    raw = pool.view(torch.int16)
+    touched_rows = int((raw != SENT16).any(dim=-1).sum())
+    assert touched_rows == w.T, f"{touched_rows} pool rows changed, expected {w.T}"
+    ref = oracle.latent_forward(w.qkv, "bf16", w.positions, w.k_norm_w, w.eps, w.theta, 512, 64)
+    got = to_host_bits(pool[pt, ot])
+    assert_close(got[:, :512], ref[:, :512], "bf16", "pool normed part")
+    assert_close(got[:, 512:], ref[:, 512:], "bf16", "pool rotated part")
+
+
+# ------------------------------------------------------------------ full-size workloads (sampled)
+
+
+@pytest.mark.parametrize("rope", [True, False], ids=["rope", "nope"])
+def test_muse_prefill_16k_sampled(rope):
+    w = prefill_interleaved(16384, rope=rope)
+    got = _gpu_forward(w, pad=256)
+    toks = _sample_tokens(w.T, 64, seed=1 if rope else 2)
+    _check_forward(w, got, tokens=toks)
+    # v everywhere, and q/k finite everywhere
+    _, _, vb = oracle.split(w.qkv, "interleaved", 16, 8, 64)
+    assert_bits_equal(got[2], vb, "prefill v (all tokens)")
+
+
+def test_qwen3_train_16k_fwd_bwd():
+    w = train_sectioned(16384)
+    got = _gpu_forward(w, pad=256)
+    toks = _sample_tokens(w.T, 48, seed=3)
+    _check_forward(w, got, tokens=toks)
+    dqkv, dwq, dwk = _gpu_backward(w)
+    ref = oracle.backward_gqa(w.qkv, w.dtype, w.kind, w.n_kv, w.q_per_kv, w.head_dim, w.positions, w.q_norm_w,
+                              w.k_norm_w, w.eps, w.theta, w.dq, w.dk, w.dv, chunk=2048)
+    _check_backward(w, dqkv, dwq, dwk, tokens=toks, ref=ref)
+    # dv lands in every token's v slots unchanged
+    _, _, gv = oracle.split(dqkv, "sectioned", 8, 4, 128)
+    assert_bits_equal(gv, w.dv, "train dv slots (all tokens)")
+
+
+# ------------------------------------------------------------------ HIP graphs
+
+
+def test_graph_replays_match_eager():
+    # forward + backward captured once, replayed several times with eager work and
+    # synchronisations in between; each replay must reproduce the eager results
+    w = custom_gqa("sectioned", "bf16", 512, 8, 4, 128, seed=21, positions="random", grads=True)
+    qkv, pos, wq, wk = _dev_inputs(w)
+    dq, dk, dv = to_dev(w.dq, "bf16"), to_dev(w.dk, "bf16"), to_dev(w.dv, "bf16")
+    kw = dict(kind="sectioned", n_kv=8, q_per_kv=4, head_dim=128, eps=w.eps, theta=w.theta)
+    outs = (torch.empty((512, 32, 128), dtype=torch.bfloat16, device="cuda"),
+            torch.empty((512, 8, 128), dtype=torch.bfloat16, device="cuda"),
+            torch.empty((512, 8, 128), dtype=torch.bfloat16, device="cuda"))
+    bouts = (torch.empty_like(qkv), torch.empty(128, device="cuda"), torch.empty(128, device="cuda"))
+    qk.forward(qkv, pos, wq, wk, out=outs, **kw)
+    qk.backward(qkv, pos, wq, wk, dq, dk, dv, out=bouts, **kw)
+    torch.cuda.synchronize()
+    ref = [to_host_bits(t) for t in outs + bouts[:1]]
+    ref_dw = [t.cpu().numpy() for t in bouts[1:]]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        qk.forward(qkv, pos, wq, wk, out=outs, **kw)
+        qk.backward(qkv, pos, wq, wk, dq, dk, dv, out=bouts, **kw)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        qk.forward(qkv, pos, wq, wk, out=outs, **kw)
+        qk.backward(qkv, pos, wq, wk, dq, dk, dv, out=bouts, **kw)
+    for r in range(4):
+        for t in outs + bouts:
+            t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32).fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, exp, n in zip([to_host_bits(t) for t in outs + bouts[:1]], ref, ["q", "k", "v", "dqkv"]):
+            assert_bits_equal(got, exp, f"replay {r} {n}")
+        for got, exp in zip([t.cpu().numpy() for t in bouts[1:]], ref_dw):
+            assert np.allclose(got, exp, rtol=1e-5, atol=1e-5 * np.abs(exp).max())
