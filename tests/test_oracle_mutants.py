@@ -1,0 +1,78 @@
+"""The oracle's pins catch plausible mistakes (CPU only).
+
+Each case plants one mistake in a temporary copy of ``oracle/reference.py``
+(a dropped term, a wrong sign, a wrong index, a swapped operand) and runs the
+pin suite against that copy in a subprocess: the suite must fail.  Nothing
+here touches the GPU or the HIP library.
+"""
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "reference.py")
+
+MUTANTS = {
+    "eps_dropped": ("return x / np.sqrt(ms + eps) * w", "return x / np.sqrt(ms) * w"),
+    "weight_dropped": ("return x / np.sqrt(ms + eps) * w", "return x / np.sqrt(ms + eps)"),
+    "rope_sign_flipped": ("return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)",
+                          "return np.concatenate([a * c + b * s, b * c - a * s], axis=-1)"),
+    "rope_pairs_adjacent": ("a, b = x[..., :h], x[..., h:]", "a, b = x[..., 0::2], x[..., 1::2]"),
+    "frequency_index": ("inv_freq = np.float64(theta) ** (-2.0 * i / R)",
+                        "inv_freq = np.float64(theta) ** (-1.0 * i / R)"),
+    "k_v_swapped": ("k[:, g, :] = X[:, g, q_per_kv, :]\n            v[:, g, :] = X[:, g, q_per_kv + 1, :]",
+                    "k[:, g, :] = X[:, g, q_per_kv + 1, :]\n            v[:, g, :] = X[:, g, q_per_kv, :]"),
+    "q_head_map_transposed": ("q[:, g * q_per_kv + s, :] = X[:, g, s, :]\n            k[:, g, :]",
+                              "q[:, s * n_kv + g, :] = X[:, g, s, :]\n            k[:, g, :]"),
+    "sectioned_k_v_swapped": ("k = X[:, n_q:n_q + n_kv, :].copy()\n        v = X[:, n_q + n_kv:, :].copy()",
+                              "v = X[:, n_q:n_q + n_kv, :].copy()\n        k = X[:, n_q + n_kv:, :].copy()"),
+    "norm_over_whole_row": ("ms = np.mean(x * x, axis=-1, keepdims=True)\n    return",
+                            "ms = np.mean(x * x, axis=(-2, -1), keepdims=True)\n    return"),
+    "bwd_projection_term_dropped": ("dx = r * (a - xhat * np.mean(a * xhat, axis=-1, keepdims=True))",
+                                    "dx = r * a"),
+    "bwd_rotation_not_inverted": ("u = g if phi is None else rope_rotate_half_inverse(g, phi)",
+                                  "u = g if phi is None else rope_rotate_half(g, phi)"),
+    "bwd_weight_dropped": ("a = w * u", "a = u"),
+    "wgrad_uses_raw_x": ("return dx, u * xhat", "return dx, u * x"),
+    "latent_rope_part_normed": ("kr = rope_rotate_half(kpe, rope_angles(pos, theta, rope_dim))",
+                                "kr = rope_rotate_half(rmsnorm(kpe, 1.0, eps), rope_angles(pos, theta, rope_dim))"),
+    "paged_offset_off_by_one": ("return page, pos % page_size", "return page, (pos + 1) % page_size"),
+    "rounding_truncates": ("r = (u + np.uint64((1 << 44) - 1) + keep_lsb) >> np.uint64(45)",
+                           "r = u >> np.uint64(45)"),
+}
+
+
+def _run(name, old, new, tmp):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"{name}: anchor not found exactly once"
+    d = os.path.join(tmp, name)
+    shutil.copytree(os.path.join(ROOT, "oracle"), os.path.join(d, "oracle"),
+                    ignore=shutil.ignore_patterns("__pycache__"))
+    with open(os.path.join(d, "oracle", "reference.py"), "w") as f:
+        f.write(src.replace(old, new))
+    env = dict(os.environ, PYTHONPATH=d + os.pathsep + ROOT, PYTHONDONTWRITEBYTECODE="1")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=d, env=env, capture_output=True, text=True, timeout=600)
+    return name, r.returncode, (r.stdout.strip().splitlines() or [""])[-1]
+
+
+def test_every_planted_mistake_fails_a_pin(tmp_path):
+    with ThreadPoolExecutor(max_workers=4) as ex:
+        results = list(ex.map(lambda kv: _run(kv[0], *kv[1], str(tmp_path)), MUTANTS.items()))
+    survivors = [(n, tail) for n, rc, tail in results if rc != 1]
+    assert not survivors, f"mistakes no pin caught (or the run broke): {survivors}"
+
+
+def test_unmutated_copy_passes(tmp_path):
+    # the harness itself: the same run on an unchanged copy must pass
+    name, rc, tail = _run("unchanged", "def head_blocks(", "def head_blocks(", str(tmp_path))
+    assert rc == 0, tail
+
+
+if __name__ == "__main__":
+    sys.exit(pytest.main([__file__, "-q"]))
