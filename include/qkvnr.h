@@ -148,14 +148,30 @@ int qkvnr_forward(const qkvnr_layout* layout, const void* qkv, const int32_t* po
  *   dqkv       out, packed like qkv (row stride in_row_stride); its v slots are
  *              a bit-exact copy of dv.
  *   dq_norm_w  out [head_dim] fp32, dk_norm_w out [head_dim] fp32: overwritten
- *              (zeroed on `stream`, then accumulated with fp32 atomics, so the
- *              last bits may differ from run to run).
+ *              with the sums over all tokens and heads.  Block partial sums are
+ *              combined with fp32 atomics into 64 workspace slots, so the last
+ *              bits may differ from run to run; a second small launch on
+ *              `stream` folds the slots into the outputs.
+ *   workspace  device scratch of at least qkvnr_backward_workspace_bytes(layout)
+ *              bytes, 16-byte aligned, owned by the caller.  It must be all
+ *              zero before its first use; every call that completes leaves it
+ *              all zero again, so one zero-filled buffer serves any number of
+ *              calls in sequence.  Calls that may run at the same time (on
+ *              different streams) need different workspaces.  After a call
+ *              that did not complete (a device fault), zero it again.  It may
+ *              be NULL when T == 0.
  * LATENT is QKVNR_EUNSUPPORTED.
  */
 int qkvnr_backward(const qkvnr_layout* layout, const void* qkv, const int32_t* positions,
                    const void* q_norm_w, const void* k_norm_w, float eps, double theta,
                    const void* dq, const void* dk, const void* dv, void* dqkv,
-                   float* dq_norm_w, float* dk_norm_w, hipStream_t stream);
+                   float* dq_norm_w, float* dk_norm_w, void* workspace, int64_t workspace_bytes,
+                   hipStream_t stream);
+
+/* Bytes of workspace qkvnr_backward needs for `layout` (at most
+ * QKVNR_BACKWARD_WORKSPACE_MAX for any supported layout). */
+int64_t qkvnr_backward_workspace_bytes(const qkvnr_layout* layout);
+#define QKVNR_BACKWARD_WORKSPACE_MAX 65536
 
 /*
  * Forward that stores k and v (GQA kinds) or the latent row (LATENT) straight

@@ -20,6 +20,7 @@ from ._binding import (  # noqa: F401
     Layout,
     QkvnrError,
     backward,
+    backward_workspace,
     forward,
     forward_latent,
     forward_latent_paged,
@@ -29,6 +30,7 @@ from ._binding import (  # noqa: F401
     latent_layout,
     lib,
     qkvnr_backward,
+    qkvnr_backward_workspace_bytes,
     qkvnr_forward,
     qkvnr_forward_paged,
     qkvnr_version,

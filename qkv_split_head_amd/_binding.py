@@ -67,8 +67,10 @@ def lib() -> ctypes.CDLL:
         L.qkvnr_forward.argtypes = [lp, vp, i32p, vp, vp, ctypes.c_float, ctypes.c_double, vp, vp, vp, vp]
         L.qkvnr_forward.restype = ctypes.c_int
         L.qkvnr_backward.argtypes = [lp, vp, i32p, vp, vp, ctypes.c_float, ctypes.c_double, vp, vp, vp, vp,
-                                     f32p, f32p, vp]
+                                     f32p, f32p, vp, ctypes.c_int64, vp]
         L.qkvnr_backward.restype = ctypes.c_int
+        L.qkvnr_backward_workspace_bytes.argtypes = [lp]
+        L.qkvnr_backward_workspace_bytes.restype = ctypes.c_int64
         L.qkvnr_forward_paged.argtypes = [lp, vp, i32p, vp, vp, ctypes.c_float, ctypes.c_double, i32p,
                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                           vp, vp, vp, vp]
@@ -117,11 +119,38 @@ def qkvnr_forward(layout: Layout, qkv, positions, q_norm_w, k_norm_w, eps: float
 
 
 def qkvnr_backward(layout: Layout, qkv, positions, q_norm_w, k_norm_w, eps: float, theta: float, dq, dk, dv,
-                   dqkv, dq_norm_w, dk_norm_w, stream=None) -> None:
+                   dqkv, dq_norm_w, dk_norm_w, workspace, workspace_bytes: int, stream=None) -> None:
     """Call ``qkvnr_backward``."""
     _check(lib().qkvnr_backward(ctypes.byref(layout), _ptr(qkv), _ptr(positions), _ptr(q_norm_w), _ptr(k_norm_w),
                                 eps, theta, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dqkv), _ptr(dq_norm_w),
-                                _ptr(dk_norm_w), _stream(stream)))
+                                _ptr(dk_norm_w), _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def qkvnr_backward_workspace_bytes(layout: Layout) -> int:
+    return lib().qkvnr_backward_workspace_bytes(ctypes.byref(layout))
+
+
+_workspaces = {}
+
+
+def backward_workspace(device=None) -> torch.Tensor:
+    """The zero-filled backward workspace this module keeps for a device.
+
+    Every completed backward call leaves it zero again, so calls issued in
+    sequence can share it.  Calls that may overlap (different streams) must
+    pass workspaces of their own.  Allocated on first use, which must not
+    happen during HIP-graph capture.
+    """
+    dev = torch.device("cuda", torch.cuda.current_device() if device is None else torch.device(device).index)
+    ws = _workspaces.get(dev.index)
+    if ws is None:
+        if torch.cuda.is_current_stream_capturing():
+            raise RuntimeError("the backward workspace is allocated on first use: run one backward call "
+                               "before capturing it in a graph, or pass workspace=")
+        size = lib().qkvnr_backward_workspace_bytes(None)
+        ws = torch.zeros(size, dtype=torch.uint8, device=dev)
+        _workspaces[dev.index] = ws
+    return ws
 
 
 def qkvnr_forward_paged(layout: Layout, qkv, positions, q_norm_w, k_norm_w, eps: float, theta: float,
@@ -184,7 +213,8 @@ def forward(qkv: torch.Tensor, positions: Optional[torch.Tensor], q_norm_w: torc
 
 def backward(qkv: torch.Tensor, positions: Optional[torch.Tensor], q_norm_w: torch.Tensor, k_norm_w: torch.Tensor,
              dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor, *, kind: str, n_kv: int, q_per_kv: int,
-             head_dim: int, rope: bool = True, eps: float = 1e-6, theta: float = 10000.0, out=None, stream=None):
+             head_dim: int, rope: bool = True, eps: float = 1e-6, theta: float = 10000.0, out=None,
+             workspace: Optional[torch.Tensor] = None, stream=None):
     """Packed dqkv (input layout) and fp32 norm-weight grads (dq_norm_w, dk_norm_w)."""
     L = gqa_layout(qkv, kind, n_kv, q_per_kv, head_dim, rope)
     if out is None:
@@ -193,7 +223,9 @@ def backward(qkv: torch.Tensor, positions: Optional[torch.Tensor], q_norm_w: tor
         dwk = torch.empty(head_dim, dtype=torch.float32, device=qkv.device)
     else:
         dqkv, dwq, dwk = out
-    qkvnr_backward(L, qkv, positions, q_norm_w, k_norm_w, eps, theta, dq, dk, dv, dqkv, dwq, dwk, stream)
+    ws = backward_workspace(qkv.device) if workspace is None else workspace
+    qkvnr_backward(L, qkv, positions, q_norm_w, k_norm_w, eps, theta, dq, dk, dv, dqkv, dwq, dwk, ws,
+                   ws.numel() * ws.element_size(), stream)
     return dqkv, dwq, dwk
 
 

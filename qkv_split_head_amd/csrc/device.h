@@ -123,19 +123,23 @@ __device__ __forceinline__ uint4 pack(const float (&f)[4]) {
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 
-// ---------------------------------------------------------------- RoPE angles
-
-// 1 / (2 pi), rounded to double.
-constexpr double kInv2Pi = 0.15915494309189533577;
-
-// Frequency of rotate-half pair f in turns per position: theta^(-2f/R) / (2 pi).
-__device__ __forceinline__ double turns_per_position(int f, int R, double log2_theta) {
-  return exp2(-(2.0 * f / R) * log2_theta) * kInv2Pi;
+// Streaming variants: the same 16-byte access with the non-temporal hint.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16_nt(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st16_nt(void* p, const uint4& v) {
+  const u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
 }
 
-// cos and sin of the angle p * theta^(-2f/R).  The product is formed in fp64
-// (p < 2^31, so the angle keeps ~1e-11 rad at any position), reduced to
-// (-1/2, 1/2] turns exactly in fp64, and only then evaluated in fp32.
+// ---------------------------------------------------------------- RoPE angles
+
+// cos and sin of the angle 2 pi * p * turns_per_pos, where turns_per_pos is
+// theta^(-2f/R) / (2 pi) for pair f (tabled on the host).  The product is
+// formed in fp64 (p < 2^31, so the angle keeps ~1e-10 rad at any position),
+// reduced to (-1/2, 1/2] turns exactly in fp64, and only then evaluated in fp32.
 __device__ __forceinline__ void rope_cos_sin(int32_t p, double turns_per_pos, float& c, float& s) {
   const double t = static_cast<double>(p) * turns_per_pos;
   const double fr = t - rint(t);

@@ -2,13 +2,18 @@
 //
 // Work decomposition.  The packed row of one token is a sequence of `heads`
 // head blocks of D values (n_q + 2 n_kv blocks; the layout decides which block
-// is which head).  A wave walks a token's row in iterations of HPI whole heads
-// (64 lanes x 16 bytes = 1 KiB per load instruction, fully coalesced); a work
-// unit is one token's row, or a segment of it when there are too few tokens to
-// fill the chip.  Units are handed out grid-stride to waves.  Each unit reads
-// its position once and computes cos/sin once: lane L evaluates pair frequency
-// L mod R/2, and each lane gathers the EPC frequencies of its chunk with
-// ds_bpermute; the same values serve every head of the token.
+// is which head).  A wave iteration covers HPI whole heads: 64 lanes x 16 bytes
+// = 1 KiB per load instruction, fully coalesced.  A token's row takes `iters`
+// iterations; a work unit is U consecutive iterations of one token, and each
+// wave does exactly one unit: it issues all of its loads at once, computes the
+// token's cos/sin while they are in flight, then normalises, rotates, stores
+// and exits.  Short-lived waves keep the memory pipeline full: on gfx9-class
+// hardware one counter tracks loads and stores in issue order, so a wave that
+// looped would wait for its own earlier stores before each new batch of loads.
+//
+// cos/sin: lane L evaluates pair frequency L mod R/2 at the token's position
+// (angle formed in fp64, frequencies tabled on the host) and each lane gathers
+// the EPC frequencies of its chunk with ds_bpermute.
 //
 // Arithmetic per head (fp32): ss = sum x^2 over the head's lanes (DPP, no
 // LDS), r = 1/sqrt(ss/D + eps), n = x r w, y = n cos + (+/-) partner(n) sin,
@@ -17,13 +22,38 @@
 
 #include "device.h"
 
+#ifndef QKVNR_FWD_UNITS
+#define QKVNR_FWD_UNITS 4
+#endif
+#ifndef QKVNR_BWD_UNITS
+#define QKVNR_BWD_UNITS 4
+#endif
+#ifndef QKVNR_NT_LOADS
+#define QKVNR_NT_LOADS 1
+#endif
+#ifndef QKVNR_NT_STORES
+#define QKVNR_NT_STORES 1
+#endif
+
 namespace qkvnr {
 
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlockThreads = kWave * kWavesPerBlock;
-constexpr int kUnroll = 4;  // wave iterations whose loads are issued together
+constexpr int kFwdU = QKVNR_FWD_UNITS;  // wave iterations per forward work unit
+constexpr int kBwdU = QKVNR_BWD_UNITS;  // wave iterations per backward work unit
+constexpr int kMaxPairs = 64;           // rotate-half pairs of the widest rotated head (D = 128)
+constexpr int kWgradSlots = 64;         // backward weight-grad partial-sum slots
 
 enum : int { kInterleaved = 0, kSectioned = 1 };
+
+__device__ __forceinline__ uint4 ld_stream(const void* p) {
+  if constexpr (QKVNR_NT_LOADS) return ld16_nt(p);
+  else return ld16(p);
+}
+__device__ __forceinline__ void st_stream(void* p, const uint4& v) {
+  if constexpr (QKVNR_NT_STORES) st16_nt(p, v);
+  else st16(p, v);
+}
 
 struct GqaArgs {
   const uint8_t* qkv;  // packed input
@@ -42,25 +72,28 @@ struct GqaArgs {
   uint8_t* dqkv;
   float* dwq;
   float* dwk;
+  float* slots;         // [kWgradSlots][2 * D] partial sums, zero between calls
   float eps;
   float inv_d;
-  double log2_theta;
+  int64_t T;
+  int64_t units;        // T * units_per_token
+  uint64_t upt_magic;   // ceil(2^64 / upt) for upt > 1: unit / upt = umul64hi(unit, magic)
+  int32_t upt;          // work units per token
   int32_t kind;
   int32_t n_kv;
   int32_t q_per_kv;
   int32_t n_q;
-  int32_t heads;      // head blocks per token
-  int32_t iters;      // wave iterations per token
-  int32_t seg_iters;  // wave iterations per work unit
-  int32_t nseg;       // work units per token
-  int64_t units;      // T * nseg
-  uint32_t grp_magic; // ceil(2^32 / (q_per_kv + 2)), exact division for head < 2^16
+  int32_t heads;        // head blocks per token
+  int32_t iters;        // wave iterations per token
+  uint32_t grp_magic;   // ceil(2^32 / (q_per_kv + 2)), exact division for head < 2^16
   // paged store
   const int32_t* bt;
   int32_t bt_stride;
   int32_t tokens_per_req;
   int32_t page_size;
   int32_t num_pages;
+  // turns per position of rotate-half pair i: theta^(-2i/R) / (2 pi)
+  double turns[kMaxPairs];
 };
 
 // Which output head a packed head block is: type 0 = q, 1 = k, 2 = v, and its index.
@@ -107,81 +140,92 @@ __device__ __forceinline__ int64_t paged_slot(const int32_t* bt, int32_t bt_stri
   return static_cast<int64_t>(page) * page_size + (p - pi * page_size);
 }
 
+template <typename IO, int D>
+struct Geo {
+  static constexpr int EPC = Chunk<IO>::EPC;
+  static constexpr int LPH = D / EPC;                          // lanes per head
+  static constexpr int HPI = kWave / LPH;                      // heads per wave iteration
+  static constexpr int HB = D * static_cast<int>(sizeof(IO));  // bytes per head
+};
+
+// This wave's work unit: token t and its first iteration it0 (wave-uniform).
+__device__ __forceinline__ bool wave_unit(const GqaArgs& a, int U, int64_t& t, int& it0) {
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int64_t unit = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave;
+  if (unit >= a.units) return false;
+  t = a.upt == 1 ? unit  // one unit per token: no division (and no 2^64 magic)
+                 : static_cast<int64_t>(__umul64hi(static_cast<uint64_t>(unit), a.upt_magic));
+  it0 = static_cast<int>(unit - t * a.upt) * U;
+  return true;
+}
+
 // ------------------------------------------------------------------ forward
 
 template <typename IO, int D, bool ROPE, bool PAGED>
 __global__ __launch_bounds__(kBlockThreads) void fwd_gqa_kernel(const GqaArgs a) {
-  constexpr int EPC = Chunk<IO>::EPC;
-  constexpr int LPH = D / EPC;
-  constexpr int HPI = kWave / LPH;
-  constexpr int HB = D * static_cast<int>(sizeof(IO));  // bytes per head
+  using G = Geo<IO, D>;
+  constexpr int EPC = G::EPC, LPH = G::LPH, HPI = G::HPI, HB = G::HB, U = kFwdU;
   const int lane = threadIdx.x & (kWave - 1);
   const int li = lane & (LPH - 1);
   const int hs = lane / LPH;
   const int c = chunk_of_lane<LPH>(li);
   const int cb = c * 16;
-  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
 
+  int64_t t;
+  int it0;
+  if (!wave_unit(a, U, t, it0)) return;
+  const int n_it = min(U, a.iters - it0);
+
+  // all of the unit's loads first
+  const uint8_t* row = a.qkv + t * a.row_bytes;
+  uint4 buf[U];
+#pragma unroll
+  for (int j = 0; j < U; ++j) {
+    const int h = (it0 + j) * HPI + hs;
+    buf[j] = make_uint4(0u, 0u, 0u, 0u);
+    if (j < n_it && h < a.heads) buf[j] = ld_stream(row + h * HB + cb);
+  }
   float wq[EPC], wk[EPC];
   unpack(ld16(a.wq + cb), wq);
   unpack(ld16(a.wk + cb), wk);
-  double tpp = 0.0;
-  if constexpr (ROPE) tpp = turns_per_position(lane % (D / 2), D, a.log2_theta);
 
-  for (int64_t u = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave; u < a.units; u += nwaves) {
-    const int64_t t = a.nseg == 1 ? u : u / a.nseg;
-    const int sg = static_cast<int>(u - t * a.nseg);
-    const int it0 = sg * a.seg_iters;
-    const int it1 = min(it0 + a.seg_iters, a.iters);
+  // cos/sin and the paged slot while the loads are in flight
+  int32_t p = 0;
+  if constexpr (ROPE || PAGED) p = a.pos[t];
+  float cs[EPC], sn[EPC];
+  if constexpr (ROPE) unit_cos_sin<EPC, LPH>(p, a.turns[lane % (D / 2)], c, cs, sn);
+  int64_t kv_tok = t;
+  if constexpr (PAGED) kv_tok = paged_slot(a.bt, a.bt_stride, a.tokens_per_req, a.page_size, a.num_pages, t, p);
 
-    int32_t p = 0;
-    if constexpr (ROPE || PAGED) p = a.pos[t];
-    float cs[EPC], sn[EPC];
-    if constexpr (ROPE) unit_cos_sin<EPC, LPH>(p, tpp, c, cs, sn);
-    int64_t kv_tok = t;
-    if constexpr (PAGED) kv_tok = paged_slot(a.bt, a.bt_stride, a.tokens_per_req, a.page_size, a.num_pages, t, p);
-
-    const uint8_t* row = a.qkv + t * a.row_bytes;
-    for (int it = it0; it < it1; it += kUnroll) {
-      uint4 buf[kUnroll];
 #pragma unroll
-      for (int j = 0; j < kUnroll; ++j) {
-        const int h = (it + j) * HPI + hs;
-        buf[j] = make_uint4(0u, 0u, 0u, 0u);
-        if (it + j < it1 && h < a.heads) buf[j] = ld16(row + h * HB + cb);
-      }
+  for (int j = 0; j < U; ++j) {
+    if (j >= n_it) break;  // wave-uniform
+    const int h = (it0 + j) * HPI + hs;
+    int type, idx;
+    map_head(a, h, type, idx);
+    float x[EPC];
+    unpack(buf[j], x);
+    float ss = 0.0f;
 #pragma unroll
-      for (int j = 0; j < kUnroll; ++j) {
-        if (it + j >= it1) break;  // wave-uniform
-        const int h = (it + j) * HPI + hs;
-        int type, idx;
-        map_head(a, h, type, idx);
-        float x[EPC];
-        unpack(buf[j], x);
-        float ss = 0.0f;
+    for (int e = 0; e < EPC; ++e) ss = fmaf(x[e], x[e], ss);
+    ss = head_sum<LPH>(ss);
+    const float r = rsqrtf(ss * a.inv_d + a.eps);
+    float y[EPC];
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) ss = fmaf(x[e], x[e], ss);
-        ss = head_sum<LPH>(ss);
-        const float r = rsqrtf(ss * a.inv_d + a.eps);
-        float y[EPC];
+    for (int e = 0; e < EPC; ++e) y[e] = x[e] * r * (type == 0 ? wq[e] : wk[e]);
+    if constexpr (ROPE) {
+      float z[EPC];
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) y[e] = x[e] * r * (type == 0 ? wq[e] : wk[e]);
-        if constexpr (ROPE) {
-          float z[EPC];
+      for (int e = 0; e < EPC; ++e) z[e] = fmaf(y[e], cs[e], partner<LPH>(y[e]) * sn[e]);
 #pragma unroll
-          for (int e = 0; e < EPC; ++e) z[e] = fmaf(y[e], cs[e], partner<LPH>(y[e]) * sn[e]);
-#pragma unroll
-          for (int e = 0; e < EPC; ++e) y[e] = z[e];
-        }
-        const uint4 out = type == 2 ? buf[j] : pack(y);
-        if (h < a.heads) {
-          if (type == 0) {
-            st16(a.q + (t * a.n_q + idx) * HB + cb, out);
-          } else if (kv_tok >= 0) {
-            st16((type == 1 ? a.k : a.v) + (kv_tok * a.n_kv + idx) * HB + cb, out);
-          }
-        }
+      for (int e = 0; e < EPC; ++e) y[e] = z[e];
+    }
+    const uint4 out = type == 2 ? buf[j] : pack(y);
+    if (h < a.heads) {
+      if (type == 0) {
+        st_stream(a.q + (t * a.n_q + idx) * HB + cb, out);
+      } else if (kv_tok >= 0) {
+        st_stream((type == 1 ? a.k : a.v) + (kv_tok * a.n_kv + idx) * HB + cb, out);
       }
     }
   }
@@ -189,107 +233,104 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_gqa_kernel(const GqaArgs a)
 
 // ------------------------------------------------------------------ backward
 
-// dwq/dwk must be zero before the launch; each block adds its partial sums.
+// Weight grads: per lane over the unit, then the wave (shuffles), then the
+// block (LDS), then one fp32 atomic per value into slot (block mod 64) of the
+// workspace (64 slots cut the contention of one shared sum 64-fold);
+// wgrad_finalize_kernel then sums the slots.  No fence is needed here: a
+// device-wide fence costs an L2 write-back on a multi-XCD part.
 template <typename IO, int D, bool ROPE>
 __global__ __launch_bounds__(kBlockThreads) void bwd_gqa_kernel(const GqaArgs a) {
-  constexpr int EPC = Chunk<IO>::EPC;
-  constexpr int LPH = D / EPC;
-  constexpr int HPI = kWave / LPH;
-  constexpr int HB = D * static_cast<int>(sizeof(IO));
+  using G = Geo<IO, D>;
+  constexpr int EPC = G::EPC, LPH = G::LPH, HPI = G::HPI, HB = G::HB, U = kBwdU;
   const int lane = threadIdx.x & (kWave - 1);
   const int li = lane & (LPH - 1);
   const int hs = lane / LPH;
   const int c = chunk_of_lane<LPH>(li);
   const int cb = c * 16;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
 
-  float wq[EPC], wk[EPC];
-  unpack(ld16(a.wq + cb), wq);
-  unpack(ld16(a.wk + cb), wk);
-  double tpp = 0.0;
-  if constexpr (ROPE) tpp = turns_per_position(lane % (D / 2), D, a.log2_theta);
   float accq[EPC], acck[EPC];
 #pragma unroll
   for (int e = 0; e < EPC; ++e) accq[e] = acck[e] = 0.0f;
 
-  for (int64_t u = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave; u < a.units; u += nwaves) {
-    const int64_t t = a.nseg == 1 ? u : u / a.nseg;
-    const int sg = static_cast<int>(u - t * a.nseg);
-    const int it0 = sg * a.seg_iters;
-    const int it1 = min(it0 + a.seg_iters, a.iters);
-    float cs[EPC], sn[EPC];
-    if constexpr (ROPE) unit_cos_sin<EPC, LPH>(a.pos[t], tpp, c, cs, sn);
+  int64_t t;
+  int it0;
+  if (wave_unit(a, U, t, it0)) {  // wave-uniform; every wave still reaches the block reduction
+    const int n_it = min(U, a.iters - it0);
     const uint8_t* row = a.qkv + t * a.row_bytes;
-    uint8_t* drow = a.dqkv + t * a.row_bytes;
-
-    for (int it = it0; it < it1; it += kUnroll) {
-      uint4 xb[kUnroll], gb[kUnroll];
+    uint4 xb[U], gb[U];
 #pragma unroll
-      for (int j = 0; j < kUnroll; ++j) {
-        const int h = (it + j) * HPI + hs;
-        xb[j] = gb[j] = make_uint4(0u, 0u, 0u, 0u);
-        if (it + j < it1 && h < a.heads) {
-          int type, idx;
-          map_head(a, h, type, idx);
-          const uint8_t* g = type == 0 ? a.dq + (t * a.n_q + idx) * HB
-                                       : (type == 1 ? a.dk : a.dv) + (t * a.n_kv + idx) * HB;
-          gb[j] = ld16(g + cb);
-          if (type != 2) xb[j] = ld16(row + h * HB + cb);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < kUnroll; ++j) {
-        if (it + j >= it1) break;  // wave-uniform
-        const int h = (it + j) * HPI + hs;
-        const bool valid = h < a.heads;
+    for (int j = 0; j < U; ++j) {
+      const int h = (it0 + j) * HPI + hs;
+      xb[j] = gb[j] = make_uint4(0u, 0u, 0u, 0u);
+      if (j < n_it && h < a.heads) {
         int type, idx;
         map_head(a, h, type, idx);
-        float x[EPC], g[EPC];
-        unpack(xb[j], x);
-        unpack(gb[j], g);
-        float ss = 0.0f;
+        const uint8_t* g = type == 0 ? a.dq + (t * a.n_q + idx) * HB
+                                     : (type == 1 ? a.dk : a.dv) + (t * a.n_kv + idx) * HB;
+        gb[j] = ld_stream(g + cb);
+        if (type != 2) xb[j] = ld_stream(row + h * HB + cb);
+      }
+    }
+    float wq[EPC], wk[EPC];
+    unpack(ld16(a.wq + cb), wq);
+    unpack(ld16(a.wk + cb), wk);
+    float cs[EPC], sn[EPC];
+    if constexpr (ROPE) unit_cos_sin<EPC, LPH>(a.pos[t], a.turns[lane % (D / 2)], c, cs, sn);
+
+    uint8_t* drow = a.dqkv + t * a.row_bytes;
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) ss = fmaf(x[e], x[e], ss);
-        ss = head_sum<LPH>(ss);
-        const float r = rsqrtf(ss * a.inv_d + a.eps);
-        float uu[EPC];
-        if constexpr (ROPE) {
-          // transpose of the forward rotation: u = g cos - partner(g) * (signed sin)
+    for (int j = 0; j < U; ++j) {
+      if (j >= n_it) break;  // wave-uniform
+      const int h = (it0 + j) * HPI + hs;
+      int type, idx;
+      map_head(a, h, type, idx);
+      float x[EPC], g[EPC];
+      unpack(xb[j], x);
+      unpack(gb[j], g);
+      float ss = 0.0f;
 #pragma unroll
-          for (int e = 0; e < EPC; ++e) uu[e] = fmaf(g[e], cs[e], -partner<LPH>(g[e]) * sn[e]);
-        } else {
+      for (int e = 0; e < EPC; ++e) ss = fmaf(x[e], x[e], ss);
+      ss = head_sum<LPH>(ss);
+      const float r = rsqrtf(ss * a.inv_d + a.eps);
+      float uu[EPC];
+      if constexpr (ROPE) {
+        // transpose of the forward rotation: u = g cos - partner(g) * (signed sin)
 #pragma unroll
-          for (int e = 0; e < EPC; ++e) uu[e] = g[e];
-        }
-        float xh[EPC], av[EPC];
-        float dot = 0.0f;
+        for (int e = 0; e < EPC; ++e) uu[e] = fmaf(g[e], cs[e], -partner<LPH>(g[e]) * sn[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) uu[e] = g[e];
+      }
+      float xh[EPC], av[EPC];
+      float dot = 0.0f;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        xh[e] = x[e] * r;
+        av[e] = uu[e] * (type == 0 ? wq[e] : wk[e]);
+        dot = fmaf(av[e], xh[e], dot);
+      }
+      dot = head_sum<LPH>(dot);
+      const float m = dot * a.inv_d;
+      float dx[EPC];
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) dx[e] = r * fmaf(-xh[e], m, av[e]);
+      if (h < a.heads) {
+        // value selects, not a choice of array (that would move both
+        // accumulators to scratch); a select also keeps a v head's unused
+        // term (NaN when eps = 0) out of the sums
 #pragma unroll
         for (int e = 0; e < EPC; ++e) {
-          xh[e] = x[e] * r;
-          av[e] = uu[e] * (type == 0 ? wq[e] : wk[e]);
-          dot = fmaf(av[e], xh[e], dot);
+          const float term = uu[e] * xh[e];
+          accq[e] += type == 0 ? term : 0.0f;
+          acck[e] += type == 1 ? term : 0.0f;
         }
-        dot = head_sum<LPH>(dot);
-        const float m = dot * a.inv_d;
-        float dx[EPC];
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) dx[e] = r * fmaf(-xh[e], m, av[e]);
-        if (valid) {
-#pragma unroll
-          for (int e = 0; e < EPC; ++e) {
-            const float term = uu[e] * xh[e];
-            if (type == 0) accq[e] += term;
-            else if (type == 1) acck[e] += term;
-          }
-          st16(drow + h * HB + cb, type == 2 ? gb[j] : pack(dx));
-        }
+        st_stream(drow + h * HB + cb, type == 2 ? gb[j] : pack(dx));
       }
     }
   }
 
-  // norm-weight grads: lanes holding the same chunk (same li) -> lanes 0..LPH-1,
-  // then the block's waves through LDS, then one atomic add per value per block.
+  // lanes holding the same chunk (same li) -> lanes 0..LPH-1 of the wave
 #pragma unroll
   for (int off = LPH; off < kWave; off <<= 1) {
 #pragma unroll
@@ -307,14 +348,31 @@ __global__ __launch_bounds__(kBlockThreads) void bwd_gqa_kernel(const GqaArgs a)
     }
   }
   __syncthreads();
+  float* slot = a.slots + (blockIdx.x % kWgradSlots) * (2 * D);
   for (int i = threadIdx.x; i < 2 * D; i += kBlockThreads) {
     float s = 0.0f;
 #pragma unroll
     for (int w = 0; w < kWavesPerBlock; ++w) s += red[w][i / D][i % D];
-    atomicAdd(i < D ? a.dwq + i : a.dwk + (i - D), s);
+    atomicAdd(slot + i, s);
   }
 }
 
+// Folds the slots into dq_norm_w / dk_norm_w (fixed order over slots) and
+// zeroes them for the next call.  Runs after the backward on the same stream,
+// so the kernel boundary orders it after every block's atomics.
+__global__ __launch_bounds__(kBlockThreads) void wgrad_finalize_kernel(float* slots, float* dwq, float* dwk, int D) {
+  for (int i = threadIdx.x; i < 2 * D; i += kBlockThreads) {
+    float s = 0.0f;
+    for (int k = 0; k < kWgradSlots; ++k) {
+      s += slots[k * 2 * D + i];
+      slots[k * 2 * D + i] = 0.0f;
+    }
+    if (i < D) dwq[i] = s;
+    else dwk[i - D] = s;
+  }
+}
+
+// Weight grads of an empty batch: zero (the workspace is left as it was, zero).
 __global__ void zero2_f32_kernel(float* a, float* b, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) {
@@ -332,13 +390,13 @@ struct LatentArgs {
   const uint8_t* w;
   uint8_t* out;  // [T, 576] or pool [pages, page_size, 576]
   float eps;
-  double log2_theta;
   int64_t T;
   const int32_t* bt;
   int32_t bt_stride;
   int32_t tokens_per_req;
   int32_t page_size;
   int32_t num_pages;
+  double turns[kMaxPairs];  // turns per position of the 32 rotated pairs
 };
 
 // bf16 rows of 512 normed values (one 16-byte chunk per lane) and 64 rotated
@@ -354,7 +412,7 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_latent_kernel(const LatentA
   const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
   float w[8];
   unpack(ld16(a.w + lane * 16), w);
-  const double tpp = turns_per_position(lane % (ROPE_D / 2), ROPE_D, a.log2_theta);
+  const double tpp = a.turns[lane % (ROPE_D / 2)];
 
   for (int64_t t = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave; t < a.T; t += nwaves) {
     const uint8_t* row = a.rows + t * a.row_bytes;

@@ -168,40 +168,45 @@ int check_paged(const int32_t* bt, int32_t bt_stride, int32_t tokens_per_req, in
 
 int heads_per_iter(int32_t dtype, int32_t D) { return kWave * (16 / elem_bytes(dtype)) / D; }
 
-// Split tokens into work units and size the grid.  With at least as many tokens
-// as resident waves each unit is a whole token row; with fewer, rows are cut
-// into segments so that small batches (decode) still spread over the chip.
-int plan_gqa(GqaArgs& a, const qkvnr_layout* L, int cus, int blocks_per_cu) {
+// turns[i] = theta^(-2i/R) / (2 pi) for the R/2 rotate-half pairs, in long double.
+void fill_turns(double* turns, double theta, int R) {
+  for (int i = 0; i < kMaxPairs; ++i) turns[i] = 0.0;
+  if (R <= 0) return;
+  const long double two_pi = 6.283185307179586476925286766559005768L;
+  for (int i = 0; i < R / 2 && i < kMaxPairs; ++i)
+    turns[i] = static_cast<double>(std::pow(static_cast<long double>(theta), -2.0L * i / R) / two_pi);
+}
+
+// Fill in the GQA launch arguments that depend only on the layout and the unit size U.
+void plan_gqa(GqaArgs& a, const qkvnr_layout* L, int U, double theta) {
   const int hpi = heads_per_iter(L->dtype, L->head_dim);
+  a.T = L->T;
   a.n_kv = L->n_kv;
   a.q_per_kv = L->q_per_kv;
   a.n_q = L->n_kv * L->q_per_kv;
   a.heads = a.n_q + 2 * L->n_kv;
   a.kind = L->kind == QKVNR_INTERLEAVED ? kInterleaved : kSectioned;
   a.iters = (a.heads + hpi - 1) / hpi;
-  const int64_t target_waves = static_cast<int64_t>(cus) * 16;
-  int64_t seg = a.iters;
-  if (L->T < target_waves) {
-    seg = (static_cast<int64_t>(a.iters) * L->T + target_waves - 1) / target_waves;
-    if (seg < 1) seg = 1;
-  }
-  a.seg_iters = static_cast<int32_t>(seg);
-  a.nseg = (a.iters + a.seg_iters - 1) / a.seg_iters;
-  a.units = L->T * a.nseg;
+  a.upt = (a.iters + U - 1) / U;
+  a.units = L->T * a.upt;
+  // ceil(2^64 / upt); upt == 1 would need 2^64, so 0 marks "no division" there
+  a.upt_magic = a.upt == 1 ? 0ull
+                           : static_cast<uint64_t>(((static_cast<unsigned __int128>(1) << 64) + a.upt - 1) /
+                                                   static_cast<unsigned __int128>(a.upt));
   const uint32_t d = static_cast<uint32_t>(a.q_per_kv + 2);
   a.grp_magic = static_cast<uint32_t>((0x100000000ull + d - 1) / d);
   a.row_bytes = L->in_row_stride * elem_bytes(L->dtype);
   a.inv_d = 1.0f / static_cast<float>(L->head_dim);
-  int64_t grid = (a.units + kWavesPerBlock - 1) / kWavesPerBlock;
-  const int64_t cap = static_cast<int64_t>(cus) * blocks_per_cu;
-  if (grid > cap) grid = cap;
-  if (grid < 1) grid = 1;
-  return static_cast<int>(grid);
+  fill_turns(a.turns, theta, L->rope_dim);
+}
+
+int unit_grid(const GqaArgs& a) {
+  return static_cast<int>((a.units + kWavesPerBlock - 1) / kWavesPerBlock);
 }
 
 template <bool PAGED>
-void launch_fwd_gqa(const GqaArgs& a, int32_t dtype, int32_t D, bool rope, int grid, hipStream_t s) {
-  const dim3 g(grid), b(kBlockThreads);
+void launch_fwd_gqa(const GqaArgs& a, int32_t dtype, int32_t D, bool rope, hipStream_t s) {
+  const dim3 g(unit_grid(a)), b(kBlockThreads);
 #define QKVNR_FWD(IO, DD, R) hipLaunchKernelGGL((fwd_gqa_kernel<IO, DD, R, PAGED>), g, b, 0, s, a)
   if (dtype == QKVNR_BF16) {
     if (D == 64) { if (rope) QKVNR_FWD(uint16_t, 64, true); else QKVNR_FWD(uint16_t, 64, false); }
@@ -213,8 +218,8 @@ void launch_fwd_gqa(const GqaArgs& a, int32_t dtype, int32_t D, bool rope, int g
 #undef QKVNR_FWD
 }
 
-void launch_bwd_gqa(const GqaArgs& a, int32_t dtype, int32_t D, bool rope, int grid, hipStream_t s) {
-  const dim3 g(grid), b(kBlockThreads);
+void launch_bwd_gqa(const GqaArgs& a, int32_t dtype, int32_t D, bool rope, hipStream_t s) {
+  const dim3 g(unit_grid(a)), b(kBlockThreads);
 #define QKVNR_BWD(IO, DD, R) hipLaunchKernelGGL((bwd_gqa_kernel<IO, DD, R>), g, b, 0, s, a)
   if (dtype == QKVNR_BF16) {
     if (D == 64) { if (rope) QKVNR_BWD(uint16_t, 64, true); else QKVNR_BWD(uint16_t, 64, false); }
@@ -226,8 +231,7 @@ void launch_bwd_gqa(const GqaArgs& a, int32_t dtype, int32_t D, bool rope, int g
 #undef QKVNR_BWD
 }
 
-constexpr int kFwdBlocksPerCu = 8;
-constexpr int kBwdBlocksPerCu = 2;
+constexpr int kLatentBlocksPerCu = 8;
 
 int latent_forward(const qkvnr_layout* L, const void* qkv, const int32_t* positions, const void* k_norm_w,
                    float eps, double theta, void* out, int64_t out_bytes, const int32_t* bt, int32_t bt_stride,
@@ -249,7 +253,7 @@ int latent_forward(const qkvnr_layout* L, const void* qkv, const int32_t* positi
   a.w = static_cast<const uint8_t*>(k_norm_w);
   a.out = static_cast<uint8_t*>(out);
   a.eps = eps;
-  a.log2_theta = std::log2(theta);
+  fill_turns(a.turns, theta, L->rope_dim);
   a.T = L->T;
   a.bt = bt;
   a.bt_stride = bt_stride;
@@ -257,7 +261,7 @@ int latent_forward(const qkvnr_layout* L, const void* qkv, const int32_t* positi
   a.page_size = page_size;
   a.num_pages = num_pages;
   int64_t grid = (L->T + kWavesPerBlock - 1) / kWavesPerBlock;
-  if (grid > static_cast<int64_t>(cus) * kFwdBlocksPerCu) grid = static_cast<int64_t>(cus) * kFwdBlocksPerCu;
+  if (grid > static_cast<int64_t>(cus) * kLatentBlocksPerCu) grid = static_cast<int64_t>(cus) * kLatentBlocksPerCu;
   if (paged)
     hipLaunchKernelGGL((fwd_latent_kernel<true>), dim3(grid), dim3(kBlockThreads), 0, stream, a);
   else
@@ -292,7 +296,7 @@ int gqa_forward(const qkvnr_layout* L, const void* qkv, const int32_t* positions
   int cus = 0;
   if (int rc = current_device(&cus)) return rc;
   GqaArgs a{};
-  const int grid = plan_gqa(a, L, cus, kFwdBlocksPerCu);
+  plan_gqa(a, L, kFwdU, theta);
   a.qkv = static_cast<const uint8_t*>(qkv);
   a.pos = positions;
   a.wq = static_cast<const uint8_t*>(q_norm_w);
@@ -301,16 +305,15 @@ int gqa_forward(const qkvnr_layout* L, const void* qkv, const int32_t* positions
   a.k = static_cast<uint8_t*>(k);
   a.v = static_cast<uint8_t*>(v);
   a.eps = eps;
-  a.log2_theta = rope ? std::log2(theta) : 0.0;
   a.bt = bt;
   a.bt_stride = bt_stride;
   a.tokens_per_req = tokens_per_req;
   a.page_size = page_size;
   a.num_pages = num_pages;
   if (paged)
-    launch_fwd_gqa<true>(a, L->dtype, L->head_dim, rope, grid, stream);
+    launch_fwd_gqa<true>(a, L->dtype, L->head_dim, rope, stream);
   else
-    launch_fwd_gqa<false>(a, L->dtype, L->head_dim, rope, grid, stream);
+    launch_fwd_gqa<false>(a, L->dtype, L->head_dim, rope, stream);
   return launched("forward");
 }
 
@@ -356,9 +359,15 @@ int qkvnr_forward_paged(const qkvnr_layout* layout, const void* qkv, const int32
                      bt_stride, tokens_per_req, page_size, num_pages, true, stream);
 }
 
+int64_t qkvnr_backward_workspace_bytes(const qkvnr_layout* layout) {
+  const int64_t D = layout && layout->head_dim > 0 ? layout->head_dim : 128;
+  return static_cast<int64_t>(kWgradSlots) * 2 * D * static_cast<int64_t>(sizeof(float));
+}
+
 int qkvnr_backward(const qkvnr_layout* layout, const void* qkv, const int32_t* positions, const void* q_norm_w,
                    const void* k_norm_w, float eps, double theta, const void* dq, const void* dk, const void* dv,
-                   void* dqkv, float* dq_norm_w, float* dk_norm_w, hipStream_t stream) {
+                   void* dqkv, float* dq_norm_w, float* dk_norm_w, void* workspace, int64_t workspace_bytes,
+                   hipStream_t stream) {
   if (int rc = check_layout(layout)) return rc;
   const qkvnr_layout* L = layout;
   if (L->kind == QKVNR_LATENT) return fail(QKVNR_EUNSUPPORTED, "backward of latent rows has no kernel");
@@ -370,7 +379,7 @@ int qkvnr_backward(const qkvnr_layout* layout, const void* qkv, const int32_t* p
   const int64_t D = L->head_dim, n_q = static_cast<int64_t>(L->n_kv) * L->q_per_kv;
   if (overlaps({dq_norm_w, D * 4}, {dk_norm_w, D * 4})) return fail(QKVNR_EINVAL, "two outputs overlap");
   int cus = 0;
-  if (L->T == 0) {  // no token is read: only the weight grads are written (zero)
+  if (L->T == 0) {  // no token is read and the workspace is not touched: the weight grads are zero
     if (int rc = current_device(&cus)) return rc;
     hipLaunchKernelGGL(zero2_f32_kernel, dim3(1), dim3(256), 0, stream, dq_norm_w, dk_norm_w, static_cast<int>(D));
     return launched("weight-grad zeroing");
@@ -385,17 +394,20 @@ int qkvnr_backward(const qkvnr_layout* layout, const void* qkv, const int32_t* p
   if (int rc = need16(dk, "dk")) return rc;
   if (int rc = need16(dv, "dv")) return rc;
   if (int rc = need16(dqkv, "dqkv")) return rc;
+  if (int rc = need16(workspace, "workspace")) return rc;
+  const int64_t ws_need = qkvnr_backward_workspace_bytes(L);
+  if (workspace_bytes < ws_need)
+    return fail(QKVNR_EINVAL, "workspace of %lld bytes is smaller than the %lld needed", (long long)workspace_bytes,
+                (long long)ws_need);
   const int64_t kvb = L->T * L->n_kv * D * es;
   if (int rc = check_disjoint(
-          {{dqkv, L->T * L->in_row_stride * es}, {dq_norm_w, D * 4}, {dk_norm_w, D * 4}},
+          {{dqkv, L->T * L->in_row_stride * es}, {dq_norm_w, D * 4}, {dk_norm_w, D * 4}, {workspace, ws_need}},
           {{qkv, L->T * L->in_row_stride * es}, {positions, positions ? L->T * 4 : 0}, {q_norm_w, D * es},
            {k_norm_w, D * es}, {dq, L->T * n_q * D * es}, {dk, kvb}, {dv, kvb}}))
     return rc;
   if (int rc = current_device(&cus)) return rc;
-  hipLaunchKernelGGL(zero2_f32_kernel, dim3(1), dim3(256), 0, stream, dq_norm_w, dk_norm_w, static_cast<int>(D));
-  if (int rc = launched("weight-grad zeroing")) return rc;
   GqaArgs a{};
-  const int grid = plan_gqa(a, L, cus, kBwdBlocksPerCu);
+  plan_gqa(a, L, kBwdU, theta);
   a.qkv = static_cast<const uint8_t*>(qkv);
   a.pos = positions;
   a.wq = static_cast<const uint8_t*>(q_norm_w);
@@ -406,10 +418,13 @@ int qkvnr_backward(const qkvnr_layout* layout, const void* qkv, const int32_t* p
   a.dqkv = static_cast<uint8_t*>(dqkv);
   a.dwq = dq_norm_w;
   a.dwk = dk_norm_w;
+  a.slots = static_cast<float*>(workspace);
   a.eps = eps;
-  a.log2_theta = rope ? std::log2(theta) : 0.0;
-  launch_bwd_gqa(a, L->dtype, L->head_dim, rope, grid, stream);
-  return launched("backward");
+  launch_bwd_gqa(a, L->dtype, L->head_dim, rope, stream);
+  if (int rc = launched("backward")) return rc;
+  hipLaunchKernelGGL(wgrad_finalize_kernel, dim3(1), dim3(kBlockThreads), 0, stream, a.slots, dq_norm_w, dk_norm_w,
+                     static_cast<int>(D));
+  return launched("weight-grad finalize");
 }
 
 const char* qkvnr_strerror(int code) {

@@ -124,7 +124,8 @@ def test_latent_descriptor_checks():
     assert qk.lib().qkvnr_forward(ctypes.byref(f32), A, B, None, C, 1e-6, 1e4, None, Dp, None, None) == qk.EUNSUPPORTED
     n256 = _lay(kind=qk.LATENT, n_kv=1, q_per_kv=0, head_dim=0, rope_dim=64, norm_dim=256, width=320)
     assert qk.lib().qkvnr_forward(ctypes.byref(n256), A, B, None, C, 1e-6, 1e4, None, Dp, None, None) == qk.EUNSUPPORTED
-    assert qk.lib().qkvnr_backward(ctypes.byref(lat), A, B, None, C, 1e-6, 1e4, A, A, A, Dp, E, F, None) == qk.EUNSUPPORTED
+    assert qk.lib().qkvnr_backward(ctypes.byref(lat), A, B, None, C, 1e-6, 1e4, A, A, A, Dp, E, F, A + (8 << 30),
+                                   1 << 20, None) == qk.EUNSUPPORTED
 
 
 def test_latent_empty_batch():
@@ -146,16 +147,33 @@ def test_paged_argument_checks():
 def test_backward_argument_checks():
     L = _lay()
     f = qk.lib().qkvnr_backward
-    args = [A, B, C, C + 4096, 1e-6, 1e4, Dp, E, F, A + (6 << 30), A + (7 << 30), A + (7 << 30) + 4096]
-    a = list(args)
-    a[9] = 0  # dqkv NULL
-    assert f(ctypes.byref(L), *a, None) == qk.EINVAL
-    a = list(args)
-    a[10] = A + (7 << 30) + 2  # dq_norm_w misaligned
-    assert f(ctypes.byref(L), *a, None) == qk.EALIGN
-    a = list(args)
-    a[9] = A + 64  # dqkv overlaps qkv
-    assert f(ctypes.byref(L), *a, None) == qk.EINVAL
+    WS = A + (8 << 30)
+    need = qk.qkvnr_backward_workspace_bytes(L)
+    args = [A, B, C, C + 4096, 1e-6, 1e4, Dp, E, F, A + (6 << 30), A + (7 << 30), A + (7 << 30) + 4096, WS, need]
+
+    def call(**change):
+        a = list(args)
+        for i, v in change.items():
+            a[int(i[1:])] = v
+        return f(ctypes.byref(L), *a, None)
+
+    assert call(i9=0) == qk.EINVAL                       # dqkv NULL
+    assert call(i10=A + (7 << 30) + 2) == qk.EALIGN      # dq_norm_w misaligned
+    assert call(i9=A + 64) == qk.EINVAL                  # dqkv overlaps qkv
+    assert call(i12=0) == qk.EINVAL                      # workspace NULL
+    assert call(i12=WS + 8) == qk.EALIGN                 # workspace misaligned
+    assert call(i13=need - 4) == qk.EINVAL               # workspace too small
+    assert "workspace" in qk.lib().qkvnr_strerror(qk.EINVAL).decode()
+    assert call(i12=A + 4096) == qk.EINVAL               # workspace overlaps qkv
+
+
+def test_backward_workspace_size():
+    L128 = _lay(n_kv=8, q_per_kv=4, head_dim=128, rope_dim=128)
+    L64 = _lay()
+    text = open(qk._binding.HEADER).read()
+    cap = int(re.search(r"#define QKVNR_BACKWARD_WORKSPACE_MAX (\d+)", text).group(1))
+    assert qk.qkvnr_backward_workspace_bytes(L64) <= qk.qkvnr_backward_workspace_bytes(L128) == cap
+    assert qk.lib().qkvnr_backward_workspace_bytes(None) == cap
 
 
 @pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU driver is present; this case is for GPU-less hosts")
