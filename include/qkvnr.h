@@ -150,7 +150,7 @@ int qkvnr_forward(const qkvnr_layout* layout, const void* qkv, const int32_t* po
  *   dq_norm_w  out [head_dim] fp32, dk_norm_w out [head_dim] fp32: overwritten
  *              with the sums over all tokens and heads.  Block partial sums are
  *              combined with fp32 atomics into 64 workspace slots, so the last
- *              bits may differ from run to run; a second small launch on
+ *              bits may differ from run to run; a second, one-block launch on
  *              `stream` folds the slots into the outputs.
  *   workspace  device scratch of at least qkvnr_backward_workspace_bytes(layout)
  *              bytes, 16-byte aligned, owned by the caller.  It must be all

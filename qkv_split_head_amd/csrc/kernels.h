@@ -37,8 +37,15 @@
 
 namespace qkvnr {
 
-constexpr int kWavesPerBlock = 4;
+#ifndef QKVNR_BWD_WAVES_PER_BLOCK
+#define QKVNR_BWD_WAVES_PER_BLOCK 4
+#endif
+
+constexpr int kWavesPerBlock = 4;  // forward and latent kernels
 constexpr int kBlockThreads = kWave * kWavesPerBlock;
+// backward: larger blocks mean fewer block partial sums of the weight grads
+constexpr int kBwdWavesPerBlock = QKVNR_BWD_WAVES_PER_BLOCK;
+constexpr int kBwdBlockThreads = kWave * kBwdWavesPerBlock;
 constexpr int kFwdU = QKVNR_FWD_UNITS;  // wave iterations per forward work unit
 constexpr int kBwdU = QKVNR_BWD_UNITS;  // wave iterations per backward work unit
 constexpr int kMaxPairs = 64;           // rotate-half pairs of the widest rotated head (D = 128)
@@ -149,9 +156,9 @@ struct Geo {
 };
 
 // This wave's work unit: token t and its first iteration it0 (wave-uniform).
-__device__ __forceinline__ bool wave_unit(const GqaArgs& a, int U, int64_t& t, int& it0) {
+__device__ __forceinline__ bool wave_unit(const GqaArgs& a, int U, int waves_per_block, int64_t& t, int& it0) {
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-  const int64_t unit = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave;
+  const int64_t unit = static_cast<int64_t>(blockIdx.x) * waves_per_block + wave;
   if (unit >= a.units) return false;
   t = a.upt == 1 ? unit  // one unit per token: no division (and no 2^64 magic)
                  : static_cast<int64_t>(__umul64hi(static_cast<uint64_t>(unit), a.upt_magic));
@@ -173,7 +180,7 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_gqa_kernel(const GqaArgs a)
 
   int64_t t;
   int it0;
-  if (!wave_unit(a, U, t, it0)) return;
+  if (!wave_unit(a, U, kWavesPerBlock, t, it0)) return;
   const int n_it = min(U, a.iters - it0);
 
   // all of the unit's loads first
@@ -185,9 +192,8 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_gqa_kernel(const GqaArgs a)
     buf[j] = make_uint4(0u, 0u, 0u, 0u);
     if (j < n_it && h < a.heads) buf[j] = ld_stream(row + h * HB + cb);
   }
-  float wq[EPC], wk[EPC];
-  unpack(ld16(a.wq + cb), wq);
-  unpack(ld16(a.wk + cb), wk);
+  // this lane's chunk of each norm weight, kept packed until a head picks one
+  const uint4 wq_raw = ld16(a.wq + cb), wk_raw = ld16(a.wk + cb);
 
   // cos/sin and the paged slot while the loads are in flight
   int32_t p = 0;
@@ -210,9 +216,10 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_gqa_kernel(const GqaArgs a)
     for (int e = 0; e < EPC; ++e) ss = fmaf(x[e], x[e], ss);
     ss = head_sum<LPH>(ss);
     const float r = rsqrtf(ss * a.inv_d + a.eps);
-    float y[EPC];
+    float w[EPC], y[EPC];
+    unpack(type == 0 ? wq_raw : wk_raw, w);
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) y[e] = x[e] * r * (type == 0 ? wq[e] : wk[e]);
+    for (int e = 0; e < EPC; ++e) y[e] = x[e] * r * w[e];
     if constexpr (ROPE) {
       float z[EPC];
 #pragma unroll
@@ -236,10 +243,11 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_gqa_kernel(const GqaArgs a)
 // Weight grads: per lane over the unit, then the wave (shuffles), then the
 // block (LDS), then one fp32 atomic per value into slot (block mod 64) of the
 // workspace (64 slots cut the contention of one shared sum 64-fold);
-// wgrad_finalize_kernel then sums the slots.  No fence is needed here: a
-// device-wide fence costs an L2 write-back on a multi-XCD part.
+// wgrad_fold_kernel then sums the slots.  A single-launch hand-over (the last
+// block to finish folds) would need every block to wait for returning atomics
+// or to fence, which costs more than the second launch on a multi-XCD part.
 template <typename IO, int D, bool ROPE>
-__global__ __launch_bounds__(kBlockThreads) void bwd_gqa_kernel(const GqaArgs a) {
+__global__ __launch_bounds__(kBwdBlockThreads) void bwd_gqa_kernel(const GqaArgs a) {
   using G = Geo<IO, D>;
   constexpr int EPC = G::EPC, LPH = G::LPH, HPI = G::HPI, HB = G::HB, U = kBwdU;
   const int lane = threadIdx.x & (kWave - 1);
@@ -255,7 +263,7 @@ __global__ __launch_bounds__(kBlockThreads) void bwd_gqa_kernel(const GqaArgs a)
 
   int64_t t;
   int it0;
-  if (wave_unit(a, U, t, it0)) {  // wave-uniform; every wave still reaches the block reduction
+  if (wave_unit(a, U, kBwdWavesPerBlock, t, it0)) {  // wave-uniform; every wave reaches the block reduction
     const int n_it = min(U, a.iters - it0);
     const uint8_t* row = a.qkv + t * a.row_bytes;
     uint4 xb[U], gb[U];
@@ -272,9 +280,7 @@ __global__ __launch_bounds__(kBlockThreads) void bwd_gqa_kernel(const GqaArgs a)
         if (type != 2) xb[j] = ld_stream(row + h * HB + cb);
       }
     }
-    float wq[EPC], wk[EPC];
-    unpack(ld16(a.wq + cb), wq);
-    unpack(ld16(a.wk + cb), wk);
+    const uint4 wq_raw = ld16(a.wq + cb), wk_raw = ld16(a.wk + cb);
     float cs[EPC], sn[EPC];
     if constexpr (ROPE) unit_cos_sin<EPC, LPH>(a.pos[t], a.turns[lane % (D / 2)], c, cs, sn);
 
@@ -302,12 +308,13 @@ __global__ __launch_bounds__(kBlockThreads) void bwd_gqa_kernel(const GqaArgs a)
 #pragma unroll
         for (int e = 0; e < EPC; ++e) uu[e] = g[e];
       }
-      float xh[EPC], av[EPC];
+      float w[EPC], xh[EPC], av[EPC];
+      unpack(type == 0 ? wq_raw : wk_raw, w);
       float dot = 0.0f;
 #pragma unroll
       for (int e = 0; e < EPC; ++e) {
         xh[e] = x[e] * r;
-        av[e] = uu[e] * (type == 0 ? wq[e] : wk[e]);
+        av[e] = uu[e] * w[e];
         dot = fmaf(av[e], xh[e], dot);
       }
       dot = head_sum<LPH>(dot);
@@ -339,7 +346,7 @@ __global__ __launch_bounds__(kBlockThreads) void bwd_gqa_kernel(const GqaArgs a)
       acck[e] += __shfl_xor(acck[e], off, kWave);
     }
   }
-  __shared__ float red[kWavesPerBlock][2][D];
+  __shared__ float red[kBwdWavesPerBlock][2][D];
   if (hs == 0) {
 #pragma unroll
     for (int e = 0; e < EPC; ++e) {
@@ -349,24 +356,41 @@ __global__ __launch_bounds__(kBlockThreads) void bwd_gqa_kernel(const GqaArgs a)
   }
   __syncthreads();
   float* slot = a.slots + (blockIdx.x % kWgradSlots) * (2 * D);
-  for (int i = threadIdx.x; i < 2 * D; i += kBlockThreads) {
+  for (int i = threadIdx.x; i < 2 * D; i += kBwdBlockThreads) {
     float s = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kWavesPerBlock; ++w) s += red[w][i / D][i % D];
+    for (int w = 0; w < kBwdWavesPerBlock; ++w) s += red[w][i / D][i % D];
     atomicAdd(slot + i, s);
   }
 }
 
-// Folds the slots into dq_norm_w / dk_norm_w (fixed order over slots) and
-// zeroes them for the next call.  Runs after the backward on the same stream,
-// so the kernel boundary orders it after every block's atomics.
-__global__ __launch_bounds__(kBlockThreads) void wgrad_finalize_kernel(float* slots, float* dwq, float* dwk, int D) {
-  for (int i = threadIdx.x; i < 2 * D; i += kBlockThreads) {
-    float s = 0.0f;
-    for (int k = 0; k < kWgradSlots; ++k) {
-      s += slots[k * 2 * D + i];
-      slots[k * 2 * D + i] = 0.0f;
-    }
+// Folds the slots into dq_norm_w / dk_norm_w and zeroes them for the next
+// call.  Launched right after the backward on the same stream, so the kernel
+// boundary orders it after every block's atomics.  One block of kFoldThreads:
+// thread (q, i) sums slots q, q + Q, ... of value i (Q = kFoldThreads / 2D,
+// all of its loads issued at once), then the Q partials of each value are
+// added in a fixed order.
+constexpr int kFoldThreads = 1024;
+template <int D>
+__global__ __launch_bounds__(kFoldThreads) void wgrad_fold_kernel(float* slots, float* dwq, float* dwk) {
+  constexpr int n = 2 * D;
+  constexpr int Q = kFoldThreads / n;  // 4 for D = 128, 8 for D = 64
+  constexpr int PER = kWgradSlots / Q;
+  __shared__ float part[kFoldThreads];
+  const int i = threadIdx.x % n, q = threadIdx.x / n;
+  float v[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) v[j] = slots[(q + j * Q) * n + i];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) slots[(q + j * Q) * n + i] = 0.0f;
+  float s = 0.0f;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) s += v[j];
+  part[threadIdx.x] = s;
+  __syncthreads();
+  if (q == 0) {
+#pragma unroll
+    for (int r = 1; r < Q; ++r) s += part[r * n + i];
     if (i < D) dwq[i] = s;
     else dwk[i - D] = s;
   }

@@ -200,13 +200,13 @@ void plan_gqa(GqaArgs& a, const qkvnr_layout* L, int U, double theta) {
   fill_turns(a.turns, theta, L->rope_dim);
 }
 
-int unit_grid(const GqaArgs& a) {
-  return static_cast<int>((a.units + kWavesPerBlock - 1) / kWavesPerBlock);
+int unit_grid(const GqaArgs& a, int waves_per_block) {
+  return static_cast<int>((a.units + waves_per_block - 1) / waves_per_block);
 }
 
 template <bool PAGED>
 void launch_fwd_gqa(const GqaArgs& a, int32_t dtype, int32_t D, bool rope, hipStream_t s) {
-  const dim3 g(unit_grid(a)), b(kBlockThreads);
+  const dim3 g(unit_grid(a, kWavesPerBlock)), b(kBlockThreads);
 #define QKVNR_FWD(IO, DD, R) hipLaunchKernelGGL((fwd_gqa_kernel<IO, DD, R, PAGED>), g, b, 0, s, a)
   if (dtype == QKVNR_BF16) {
     if (D == 64) { if (rope) QKVNR_FWD(uint16_t, 64, true); else QKVNR_FWD(uint16_t, 64, false); }
@@ -219,7 +219,7 @@ void launch_fwd_gqa(const GqaArgs& a, int32_t dtype, int32_t D, bool rope, hipSt
 }
 
 void launch_bwd_gqa(const GqaArgs& a, int32_t dtype, int32_t D, bool rope, hipStream_t s) {
-  const dim3 g(unit_grid(a)), b(kBlockThreads);
+  const dim3 g(unit_grid(a, kBwdWavesPerBlock)), b(kBwdBlockThreads);
 #define QKVNR_BWD(IO, DD, R) hipLaunchKernelGGL((bwd_gqa_kernel<IO, DD, R>), g, b, 0, s, a)
   if (dtype == QKVNR_BF16) {
     if (D == 64) { if (rope) QKVNR_BWD(uint16_t, 64, true); else QKVNR_BWD(uint16_t, 64, false); }
@@ -422,9 +422,11 @@ int qkvnr_backward(const qkvnr_layout* layout, const void* qkv, const int32_t* p
   a.eps = eps;
   launch_bwd_gqa(a, L->dtype, L->head_dim, rope, stream);
   if (int rc = launched("backward")) return rc;
-  hipLaunchKernelGGL(wgrad_finalize_kernel, dim3(1), dim3(kBlockThreads), 0, stream, a.slots, dq_norm_w, dk_norm_w,
-                     static_cast<int>(D));
-  return launched("weight-grad finalize");
+  if (D == 64)
+    hipLaunchKernelGGL(wgrad_fold_kernel<64>, dim3(1), dim3(kFoldThreads), 0, stream, a.slots, dq_norm_w, dk_norm_w);
+  else
+    hipLaunchKernelGGL(wgrad_fold_kernel<128>, dim3(1), dim3(kFoldThreads), 0, stream, a.slots, dq_norm_w, dk_norm_w);
+  return launched("weight-grad fold");
 }
 
 const char* qkvnr_strerror(int code) {

@@ -296,6 +296,18 @@ def test_backward_workspace_is_left_zero():
                     dwk.cpu().numpy().astype(np.float64))
 
 
+def test_backward_calls_of_changing_size_share_one_workspace():
+    # grid sizes change call to call; the last block of each call must fold the
+    # slots and leave the shared workspace zero for the next
+    ws = qk.backward_workspace()
+    for i, (kind, T, n_kv, Q, D) in enumerate([("sectioned", 700, 8, 4, 128), ("interleaved", 5, 16, 8, 64),
+                                               ("interleaved", 1, 2, 2, 64), ("sectioned", 3001, 2, 3, 128),
+                                               ("interleaved", 64, 3, 5, 64)]):
+        w = custom_gqa(kind, "bf16", T, n_kv, Q, D, theta=1e6, seed=40 + i, positions="random", grads=True)
+        _check_backward(w, *_gpu_backward(w))
+        assert int(ws.count_nonzero()) == 0, f"workspace not left zero after call {i}"
+
+
 def test_backward_padded_row_stride_leaves_padding():
     w = custom_gqa("interleaved", "bf16", 77, 2, 4, 64, seed=8, positions="random", grads=True)
     width = w.width
