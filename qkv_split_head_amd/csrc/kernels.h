@@ -25,8 +25,14 @@
 #ifndef QKVNR_FWD_UNITS
 #define QKVNR_FWD_UNITS 4
 #endif
+#ifndef QKVNR_FWD_DEPTH
+#define QKVNR_FWD_DEPTH 3
+#endif
 #ifndef QKVNR_BWD_UNITS
 #define QKVNR_BWD_UNITS 4
+#endif
+#ifndef QKVNR_BWD_DEPTH
+#define QKVNR_BWD_DEPTH QKVNR_BWD_UNITS
 #endif
 #ifndef QKVNR_NT_LOADS
 #define QKVNR_NT_LOADS 1
@@ -47,7 +53,11 @@ constexpr int kBlockThreads = kWave * kWavesPerBlock;
 constexpr int kBwdWavesPerBlock = QKVNR_BWD_WAVES_PER_BLOCK;
 constexpr int kBwdBlockThreads = kWave * kBwdWavesPerBlock;
 constexpr int kFwdU = QKVNR_FWD_UNITS;  // wave iterations per forward work unit
+constexpr int kFwdDepth = QKVNR_FWD_DEPTH;  // forward streaming loads in flight per wave
 constexpr int kBwdU = QKVNR_BWD_UNITS;  // wave iterations per backward work unit
+constexpr int kBwdDepth = QKVNR_BWD_DEPTH;  // backward iterations whose loads are in flight per wave
+static_assert(kFwdDepth >= 1 && kFwdDepth <= kFwdU, "forward load depth must be in [1, units]");
+static_assert(kBwdDepth >= 1 && kBwdDepth <= kBwdU, "backward load depth must be in [1, units]");
 constexpr int kMaxPairs = 64;           // rotate-half pairs of the widest rotated head (D = 128)
 constexpr int kWgradSlots = 64;         // backward weight-grad partial-sum slots
 
@@ -183,25 +193,30 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_gqa_kernel(const GqaArgs a)
   if (!wave_unit(a, U, kWavesPerBlock, t, it0)) return;
   const int n_it = min(U, a.iters - it0);
 
-  // all of the unit's loads first
+  // Small operands first: the vector memory counter completes in issue order,
+  // so loads issued before the streaming loads can be waited for alone.
+  // This lane's chunk of each norm weight stays packed until a head picks one.
+  const uint4 wq_raw = ld16(a.wq + cb), wk_raw = ld16(a.wk + cb);
+  double tpp = 0.0;
+  if constexpr (ROPE) tpp = a.turns[lane % (D / 2)];
+  int32_t p = 0;
+  if constexpr (ROPE || PAGED) p = a.pos[t];  // t is wave-uniform: a scalar load
+  int64_t kv_tok = t;
+  if constexpr (PAGED) kv_tok = paged_slot(a.bt, a.bt_stride, a.tokens_per_req, a.page_size, a.num_pages, t, p);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // Streaming loads without branches: a lane past the last head re-reads the
+  // last head block (same row, already in flight), and its result is dropped.
+  // kFwdDepth of them go out at once; each store is followed by the next load.
   const uint8_t* row = a.qkv + t * a.row_bytes;
   uint4 buf[U];
 #pragma unroll
-  for (int j = 0; j < U; ++j) {
-    const int h = (it0 + j) * HPI + hs;
-    buf[j] = make_uint4(0u, 0u, 0u, 0u);
-    if (j < n_it && h < a.heads) buf[j] = ld_stream(row + h * HB + cb);
-  }
-  // this lane's chunk of each norm weight, kept packed until a head picks one
-  const uint4 wq_raw = ld16(a.wq + cb), wk_raw = ld16(a.wk + cb);
+  for (int j = 0; j < kFwdDepth; ++j)
+    buf[j] = ld_stream(row + min((it0 + j) * HPI + hs, a.heads - 1) * HB + cb);
+  __builtin_amdgcn_sched_barrier(0);
 
-  // cos/sin and the paged slot while the loads are in flight
-  int32_t p = 0;
-  if constexpr (ROPE || PAGED) p = a.pos[t];
   float cs[EPC], sn[EPC];
-  if constexpr (ROPE) unit_cos_sin<EPC, LPH>(p, a.turns[lane % (D / 2)], c, cs, sn);
-  int64_t kv_tok = t;
-  if constexpr (PAGED) kv_tok = paged_slot(a.bt, a.bt_stride, a.tokens_per_req, a.page_size, a.num_pages, t, p);
+  if constexpr (ROPE) unit_cos_sin<EPC, LPH>(p, tpp, c, cs, sn);
 
 #pragma unroll
   for (int j = 0; j < U; ++j) {
@@ -228,12 +243,13 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_gqa_kernel(const GqaArgs a)
       for (int e = 0; e < EPC; ++e) y[e] = z[e];
     }
     const uint4 out = type == 2 ? buf[j] : pack(y);
-    if (h < a.heads) {
-      if (type == 0) {
-        st_stream(a.q + (t * a.n_q + idx) * HB + cb, out);
-      } else if (kv_tok >= 0) {
-        st_stream((type == 1 ? a.k : a.v) + (kv_tok * a.n_kv + idx) * HB + cb, out);
-      }
+    uint8_t* dst = type == 0 ? a.q + (t * a.n_q + idx) * HB
+                             : (type == 1 ? a.k : a.v) + (kv_tok * a.n_kv + idx) * HB;
+    if (h < a.heads && (type == 0 || kv_tok >= 0)) st_stream(dst + cb, out);
+    if (j + kFwdDepth < U) {
+      __builtin_amdgcn_sched_barrier(0);
+      buf[j + kFwdDepth] = ld_stream(row + min((it0 + j + kFwdDepth) * HPI + hs, a.heads - 1) * HB + cb);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
@@ -246,6 +262,25 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_gqa_kernel(const GqaArgs a)
 // wgrad_fold_kernel then sums the slots.  A single-launch hand-over (the last
 // block to finish folds) would need every block to wait for returning atomics
 // or to fence, which costs more than the second launch on a multi-XCD part.
+// One iteration's backward loads for the lane's head block h: its output
+// cotangent and, for q/k heads, its input.  Lanes past the last head re-read
+// the last head, and a v head, whose input is not needed, reads the q weight
+// chunk (cached) in place of its input chunk: no load is skipped, because a
+// skipped load would turn every later wait into a full drain.
+template <int HB>
+// (`a` by value: with a reference to the kernel argument block the compiler
+// copies the whole block to scratch.)
+__device__ __forceinline__ void bwd_load(const GqaArgs a, int64_t t, int h, const uint8_t* row, int cb,
+                                         uint4& xb, uint4& gb) {
+  h = min(h, a.heads - 1);
+  int type, idx;
+  map_head(a, h, type, idx);
+  const uint8_t* g = type == 0 ? a.dq + (t * a.n_q + idx) * HB
+                               : (type == 1 ? a.dk : a.dv) + (t * a.n_kv + idx) * HB;
+  gb = ld_stream(g + cb);
+  xb = ld_stream(type != 2 ? row + h * HB + cb : a.wq + cb);
+}
+
 template <typename IO, int D, bool ROPE>
 __global__ __launch_bounds__(kBwdBlockThreads) void bwd_gqa_kernel(const GqaArgs a) {
   using G = Geo<IO, D>;
@@ -265,24 +300,24 @@ __global__ __launch_bounds__(kBwdBlockThreads) void bwd_gqa_kernel(const GqaArgs
   int it0;
   if (wave_unit(a, U, kBwdWavesPerBlock, t, it0)) {  // wave-uniform; every wave reaches the block reduction
     const int n_it = min(U, a.iters - it0);
+    // small operands first (see the forward kernel)
+    const uint4 wq_raw = ld16(a.wq + cb), wk_raw = ld16(a.wk + cb);
+    double tpp = 0.0;
+    int32_t p = 0;
+    if constexpr (ROPE) {
+      tpp = a.turns[lane % (D / 2)];
+      p = a.pos[t];
+    }
+    __builtin_amdgcn_sched_barrier(0);
     const uint8_t* row = a.qkv + t * a.row_bytes;
     uint4 xb[U], gb[U];
+    // kBwdDepth iterations' loads go out at once; each store is followed by
+    // the loads of the next iteration
 #pragma unroll
-    for (int j = 0; j < U; ++j) {
-      const int h = (it0 + j) * HPI + hs;
-      xb[j] = gb[j] = make_uint4(0u, 0u, 0u, 0u);
-      if (j < n_it && h < a.heads) {
-        int type, idx;
-        map_head(a, h, type, idx);
-        const uint8_t* g = type == 0 ? a.dq + (t * a.n_q + idx) * HB
-                                     : (type == 1 ? a.dk : a.dv) + (t * a.n_kv + idx) * HB;
-        gb[j] = ld_stream(g + cb);
-        if (type != 2) xb[j] = ld_stream(row + h * HB + cb);
-      }
-    }
-    const uint4 wq_raw = ld16(a.wq + cb), wk_raw = ld16(a.wk + cb);
+    for (int j = 0; j < kBwdDepth; ++j) bwd_load<HB>(a, t, (it0 + j) * HPI + hs, row, cb, xb[j], gb[j]);
+    __builtin_amdgcn_sched_barrier(0);
     float cs[EPC], sn[EPC];
-    if constexpr (ROPE) unit_cos_sin<EPC, LPH>(a.pos[t], a.turns[lane % (D / 2)], c, cs, sn);
+    if constexpr (ROPE) unit_cos_sin<EPC, LPH>(p, tpp, c, cs, sn);
 
     uint8_t* drow = a.dqkv + t * a.row_bytes;
 #pragma unroll
@@ -334,6 +369,11 @@ __global__ __launch_bounds__(kBwdBlockThreads) void bwd_gqa_kernel(const GqaArgs
         }
         st_stream(drow + h * HB + cb, type == 2 ? gb[j] : pack(dx));
       }
+      if (j + kBwdDepth < U) {
+        __builtin_amdgcn_sched_barrier(0);
+        bwd_load<HB>(a, t, (it0 + j + kBwdDepth) * HPI + hs, row, cb, xb[j + kBwdDepth], gb[j + kBwdDepth]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
 
@@ -354,7 +394,11 @@ __global__ __launch_bounds__(kBwdBlockThreads) void bwd_gqa_kernel(const GqaArgs
       red[wave][1][c * EPC + e] = acck[e];
     }
   }
-  __syncthreads();
+  // a barrier that orders LDS only: __syncthreads() would also make every
+  // wave wait for its streaming stores to be acknowledged first
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   float* slot = a.slots + (blockIdx.x % kWgradSlots) * (2 * D);
   for (int i = threadIdx.x; i < 2 * D; i += kBwdBlockThreads) {
     float s = 0.0f;

@@ -200,6 +200,13 @@ void plan_gqa(GqaArgs& a, const qkvnr_layout* L, int U, double theta) {
   fill_turns(a.turns, theta, L->rope_dim);
 }
 
+#ifndef QKVNR_FWD_LDS
+#define QKVNR_FWD_LDS 0
+#endif
+#ifndef QKVNR_BWD_LDS
+#define QKVNR_BWD_LDS 0
+#endif
+
 int unit_grid(const GqaArgs& a, int waves_per_block) {
   return static_cast<int>((a.units + waves_per_block - 1) / waves_per_block);
 }
@@ -207,7 +214,7 @@ int unit_grid(const GqaArgs& a, int waves_per_block) {
 template <bool PAGED>
 void launch_fwd_gqa(const GqaArgs& a, int32_t dtype, int32_t D, bool rope, hipStream_t s) {
   const dim3 g(unit_grid(a, kWavesPerBlock)), b(kBlockThreads);
-#define QKVNR_FWD(IO, DD, R) hipLaunchKernelGGL((fwd_gqa_kernel<IO, DD, R, PAGED>), g, b, 0, s, a)
+#define QKVNR_FWD(IO, DD, R) hipLaunchKernelGGL((fwd_gqa_kernel<IO, DD, R, PAGED>), g, b, QKVNR_FWD_LDS, s, a)
   if (dtype == QKVNR_BF16) {
     if (D == 64) { if (rope) QKVNR_FWD(uint16_t, 64, true); else QKVNR_FWD(uint16_t, 64, false); }
     else         { if (rope) QKVNR_FWD(uint16_t, 128, true); else QKVNR_FWD(uint16_t, 128, false); }
@@ -220,7 +227,7 @@ void launch_fwd_gqa(const GqaArgs& a, int32_t dtype, int32_t D, bool rope, hipSt
 
 void launch_bwd_gqa(const GqaArgs& a, int32_t dtype, int32_t D, bool rope, hipStream_t s) {
   const dim3 g(unit_grid(a, kBwdWavesPerBlock)), b(kBwdBlockThreads);
-#define QKVNR_BWD(IO, DD, R) hipLaunchKernelGGL((bwd_gqa_kernel<IO, DD, R>), g, b, 0, s, a)
+#define QKVNR_BWD(IO, DD, R) hipLaunchKernelGGL((bwd_gqa_kernel<IO, DD, R>), g, b, QKVNR_BWD_LDS, s, a)
   if (dtype == QKVNR_BF16) {
     if (D == 64) { if (rope) QKVNR_BWD(uint16_t, 64, true); else QKVNR_BWD(uint16_t, 64, false); }
     else         { if (rope) QKVNR_BWD(uint16_t, 128, true); else QKVNR_BWD(uint16_t, 128, false); }
