@@ -194,6 +194,10 @@ def main():
 
     fwd_ms = per_launch_ms(fwd, K)
     bwd_ms = per_launch_ms(bwd, K)
+    # practical ceiling beside the 8 TB/s figure: the runtime's device copy of
+    # the packed input (the forward's byte count: read + write), same rotation
+    nxt = {id(sets[i]): sets[(i + 1) % 3] for i in range(3)}
+    copy_ms = per_launch_ms(lambda s: s["dqkv"].copy_(nxt[id(s)]["qkv"]), K)
     fwd_b, bwd_b = gqa_bytes(T, n_q, n_kv, D, 2)
     ms_per_step = wall / K * 1e3
     value = (fwd_b + bwd_b) / (ms_per_step * 1e-3) / 1e9
@@ -208,6 +212,8 @@ def main():
         "train_bwd_GBps": round(bwd_gbs, 1),
         "train_fwd_plus_bwd_us": round((fwd_ms + bwd_ms) * 1e3, 2),
         "train_algorithmic_bytes": {"fwd": fwd_b, "bwd": bwd_b},
+        "copy_ceiling_us": round(copy_ms * 1e3, 2),
+        "copy_ceiling_GBps": round(fwd_b / (copy_ms * 1e-3) / 1e9, 1),
     }
 
     if not args.no_extras:
