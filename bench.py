@@ -104,6 +104,64 @@ def cpu_baseline(target_s: float = 12.0):
     }
 
 
+def drafter_extras(dev_bf16, stream, layers_n: int = 4, n: int = 30):
+    """Per-layer decode-step time of a 4-layer MLA drafter step (distinct weights and
+    pools per layer, DeepSeek-V3-style shapes at one rank's share of TP8) under HIP
+    graph replay: serial, split (kv path on a second stream, fork/join) or merged
+    (one q_a|kv_a projection, one stream) schedules, direct or staged pool write,
+    B = 1 and 4 requests of 16 draft tokens.  Latency-bound: microseconds, no
+    bandwidth figure."""
+    import torch
+    from qkv_inputs import mla_drafter_layer
+    from qkv_split_head_amd.mla_drafter import MlaDims, MlaDrafterLayer, staged_slots
+
+    names = ("w_input_ln", "w_q_a", "w_q_a_ln", "w_q_b", "w_uk", "w_kv_a", "w_kv_a_ln")
+    ins = [mla_drafter_layer(4, 16, seed=70 + i) for i in range(layers_n)]
+    layers = [MlaDrafterLayer({k: dev_bf16(getattr(m, k)) for k in names}, MlaDims()) for m in ins]
+    pools = [torch.zeros((m.num_pages, m.page_size, 576), dtype=torch.bfloat16, device="cuda") for m in ins]
+    out = {"layers_per_step": layers_n, "graph_replays": n}
+    for B in (1, 4):
+        m0 = ins[0]
+        x = dev_bf16(m0.x[:B * 16])
+        pos = torch.from_numpy(m0.positions[:B * 16]).cuda()
+        bt = torch.from_numpy(m0.block_table[:B]).cuda()
+        res = {}
+        for split, merge in ((False, False), (True, False), (False, True)):
+            for direct in (False, True):
+                def step():
+                    # the staged write's slots: once per step, shared by the layers
+                    slots = None if direct else staged_slots(pos, bt, 16, 64, pools[0].shape[0] * 64)
+                    for lay, pool in zip(layers, pools):
+                        lay.forward(x, pos, bt, pool, 16, split_streams=split, direct_pool_write=direct,
+                                    merge_kv_a=merge, slots=slots)
+                side = torch.cuda.Stream()
+                side.wait_stream(stream)
+                with torch.cuda.stream(side):
+                    for _ in range(2):
+                        step()
+                stream.wait_stream(side)
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    step()
+                for _ in range(5):
+                    g.replay()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(n):
+                    g.replay()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                key = ("split" if split else "merged" if merge else "serial") + ("_direct" if direct else "_staged")
+                res[key] = round(e0.elapsed_time(e1) / (n * layers_n) * 1e3, 2)
+                del g
+        res["split_streams_saving_us"] = round(res["serial_direct"] - res["split_direct"], 2)
+        res["merged_projection_saving_us"] = round(res["serial_direct"] - res["merged_direct"], 2)
+        res["direct_write_saving_us"] = round(res["serial_staged"] - res["serial_direct"], 2)
+        out[f"B{B}_us_per_layer"] = res
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -301,6 +359,9 @@ def main():
         torch.cuda.synchronize()
         extras["mla_latent_paged_B4xT16_us"] = round(e0.elapsed_time(e1) / (n * CALLS) * 1e3, 2)
         del pool, g
+
+        # ------------------------------------------------------------ MLA drafter layers: kv path beside q path
+        extras["mla_drafter"] = drafter_extras(dev_bf16, stream)
 
     out = {
         "metric": METRIC,

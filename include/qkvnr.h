@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define QKVNR_VERSION 10000 /* major * 10000 + minor * 100 + patch */
+#define QKVNR_VERSION 10100 /* major * 10000 + minor * 100 + patch */
 
 /* Return codes. */
 #define QKVNR_OK 0
@@ -202,6 +202,32 @@ int qkvnr_forward_paged(const qkvnr_layout* layout, const void* qkv, const int32
                         const int32_t* block_table, int32_t bt_stride, int32_t tokens_per_req,
                         int32_t page_size, int32_t num_pages, void* q, void* k_pool,
                         void* v_pool, hipStream_t stream);
+
+/*
+ * Rotate-half RoPE, in place, of the rope part of every head of x: the q
+ * path's rotation of its heads' rope parts in the MLA drafter layer, which
+ * runs beside the latent kv path (TensorRT-LLM page: Description, the q path
+ * "q_a_proj -> q_a_layernorm -> q_b_proj -> rope_into -> k absorption").  No
+ * norm.  Same rotation and angle handling as qkvnr_forward: pairs
+ * (i, i + R/2) of the R = rope_dim values at rope_offset turn by
+ * pos * theta^(-2i/R), formed in fp64 and reduced in turns; one rounding.
+ *
+ *   dtype        QKVNR_BF16 (QKVNR_FP32 is QKVNR_EUNSUPPORTED).
+ *   T            tokens, >= 0 (T == 0 is a no-op; x and positions may be NULL).
+ *   heads        heads per token, >= 1.
+ *   token_stride elements from one token to the next (>= heads * head_stride).
+ *   head_stride  elements from one head to the next within a token.
+ *   rope_offset  first rotated element within a head; rope_offset + rope_dim
+ *                <= head_stride.  rope_offset, head_stride and token_stride
+ *                must be multiples of 8 elements (QKVNR_EALIGN otherwise).
+ *   rope_dim     64 or 128 (others QKVNR_EUNSUPPORTED).
+ *   positions    [T] int32, 4-byte aligned.
+ *   x            in/out, 16-byte aligned; only the rope parts are read and
+ *                written.  Must not overlap positions.
+ */
+int qkvnr_rope_inplace(int32_t dtype, int64_t T, int32_t heads, int64_t token_stride,
+                       int32_t head_stride, int32_t rope_offset, int32_t rope_dim,
+                       const int32_t* positions, double theta, void* x, hipStream_t stream);
 
 /* Static text for a return code.  For QKVNR_EHIP and the validation errors it
  * returns the last detailed message recorded on the calling thread. */

@@ -20,3 +20,4 @@ from .reference import (  # noqa: F401
     paged_slots,
     staged_then_scatter,
 )
+from .mla_drafter import absorb, drafter_layer  # noqa: F401,E402

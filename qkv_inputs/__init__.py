@@ -16,5 +16,7 @@ from .generators import (  # noqa: F401
     latent_paged,
     gqa_paged,
     custom_gqa,
+    MlaDrafterInputs,
+    mla_drafter_layer,
     SEEDS,
 )

@@ -28,9 +28,12 @@ def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
 
     Input preparation only: turns fp32 random draws into bf16 test tensors.
     """
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    bias = np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))
-    return ((u + bias) >> np.uint64(16)).astype(np.uint16)
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("only finite values are rounded here")
+    # finite patterns are at most 0xFF7FFFFF, so adding < 0x8001 cannot wrap
+    bias = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
 
 
 def f32_from_bf16_bits(b: np.ndarray) -> np.ndarray:
@@ -256,5 +259,86 @@ def gqa_paged(
         name=f"gqa_paged_{kind}_{dtype}_B{B}_T{T_req}", kind=kind, dtype=dtype, T=T, n_kv=n_kv,
         q_per_kv=q_per_kv, head_dim=head_dim, rope_dim=head_dim if rope else 0, eps=1e-6, theta=theta,
         qkv=qkv, positions=pos, q_norm_w=wq, k_norm_w=wk, block_table=table, tokens_per_req=T_req,
+        page_size=page_size, num_pages=num_pages, extra={"ctx": ctx},
+    )
+
+
+@dataclass
+class MlaDrafterInputs:
+    """One MLA drafter layer's decode-step inputs and random-init weights.
+
+    Matrices are stored ``[in, out]`` (a projection is ``x @ W``).  bf16 arrays
+    are ``uint16`` bit patterns.  Projection weights are N(0, 1/fan_in), so
+    every projection output is O(1); norm weights are N(1, 0.1).
+    """
+
+    name: str
+    B: int
+    T_req: int
+    hidden: int
+    q_lora_rank: int
+    kv_lora_rank: int
+    qk_nope_head_dim: int
+    qk_rope_head_dim: int
+    heads: int
+    eps: float
+    theta: float
+    x: np.ndarray             # [B*T_req, hidden], the layer input
+    w_input_ln: np.ndarray    # [hidden]
+    w_q_a: np.ndarray         # [hidden, q_lora_rank]
+    w_q_a_ln: np.ndarray      # [q_lora_rank]
+    w_q_b: np.ndarray         # [q_lora_rank, heads * (nope + rope)]
+    w_uk: np.ndarray          # [heads, nope, kv_lora_rank]
+    w_kv_a: np.ndarray        # [hidden, kv_lora_rank + rope]
+    w_kv_a_ln: np.ndarray     # [kv_lora_rank]
+    positions: np.ndarray     # [B*T_req] int32
+    block_table: np.ndarray   # [B, bt_stride] int32, -1 = unused
+    tokens_per_req: int
+    page_size: int
+    num_pages: int
+    extra: dict = field(default_factory=dict)
+
+
+def mla_drafter_layer(
+    B: int = 4,
+    T_req: int = 16,
+    *,
+    hidden: int = 7168,
+    q_lora_rank: int = 1536,
+    kv_lora_rank: int = 512,
+    qk_nope_head_dim: int = 128,
+    qk_rope_head_dim: int = 64,
+    heads: int = 16,
+    num_pages: int = 8192,
+    page_size: int = 64,
+    ctx_lo: int = 2048,
+    ctx_hi: int = 131072,
+    seed: Optional[int] = None,
+) -> MlaDrafterInputs:
+    """A DeepSeek-V3-style MLA layer at one rank's share of tensor parallelism 8
+    (128 heads / 8 = 16), B requests of T_req draft tokens after random contexts.
+
+    Draw order: layer input, input-norm weight, q_a, q_a norm weight, q_b, W_UK,
+    kv_a, kv_a norm weight, then the block table (as for the latent workload).
+    """
+    if seed is None:
+        seed = 50 + B
+    rng = np.random.Generator(np.random.PCG64(seed))
+    N = B * T_req
+    qh = qk_nope_head_dim + qk_rope_head_dim
+    x = _draw(rng, (N, hidden), "bf16")
+    w_in = _draw(rng, (hidden,), "bf16", 1.0, 0.1)
+    w_qa = _draw(rng, (hidden, q_lora_rank), "bf16", 0.0, float(hidden) ** -0.5)
+    w_qa_ln = _draw(rng, (q_lora_rank,), "bf16", 1.0, 0.1)
+    w_qb = _draw(rng, (q_lora_rank, heads * qh), "bf16", 0.0, float(q_lora_rank) ** -0.5)
+    w_uk = _draw(rng, (heads, qk_nope_head_dim, kv_lora_rank), "bf16", 0.0, float(qk_nope_head_dim) ** -0.5)
+    w_kva = _draw(rng, (hidden, kv_lora_rank + qk_rope_head_dim), "bf16", 0.0, float(hidden) ** -0.5)
+    w_kva_ln = _draw(rng, (kv_lora_rank,), "bf16", 1.0, 0.1)
+    ctx, pos, table = _block_table(rng, B, T_req, num_pages, page_size, ctx_lo, ctx_hi)
+    return MlaDrafterInputs(
+        name=f"mla_drafter_B{B}_T{T_req}", B=B, T_req=T_req, hidden=hidden, q_lora_rank=q_lora_rank,
+        kv_lora_rank=kv_lora_rank, qk_nope_head_dim=qk_nope_head_dim, qk_rope_head_dim=qk_rope_head_dim,
+        heads=heads, eps=1e-6, theta=1e4, x=x, w_input_ln=w_in, w_q_a=w_qa, w_q_a_ln=w_qa_ln, w_q_b=w_qb,
+        w_uk=w_uk, w_kv_a=w_kva, w_kv_a_ln=w_kva_ln, positions=pos, block_table=table, tokens_per_req=T_req,
         page_size=page_size, num_pages=num_pages, extra={"ctx": ctx},
     )

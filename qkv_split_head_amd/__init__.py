@@ -4,7 +4,9 @@ Python face of ``libqkvnr.so`` (C ABI in ``include/qkvnr.h``).  The functions
 named like the C entry points (``qkvnr_forward``, ``qkvnr_backward``,
 ``qkvnr_forward_paged``) pass tensors straight through; ``forward``,
 ``backward``, ``forward_paged``, ``forward_latent`` and
-``forward_latent_paged`` also allocate the outputs.
+``forward_latent_paged`` also allocate the outputs; ``rope_inplace`` rotates a
+tensor's rope parts in place.  ``mla_drafter`` runs an MLA drafter layer's kv
+path beside its q path on two streams.
 """
 from ._binding import (  # noqa: F401
     BF16,
@@ -33,5 +35,7 @@ from ._binding import (  # noqa: F401
     qkvnr_backward_workspace_bytes,
     qkvnr_forward,
     qkvnr_forward_paged,
+    qkvnr_rope_inplace,
+    rope_inplace,
     qkvnr_version,
 )

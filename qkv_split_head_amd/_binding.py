@@ -75,6 +75,10 @@ def lib() -> ctypes.CDLL:
                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                           vp, vp, vp, vp]
         L.qkvnr_forward_paged.restype = ctypes.c_int
+        L.qkvnr_rope_inplace.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int64,
+                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, i32p, ctypes.c_double,
+                                         vp, vp]
+        L.qkvnr_rope_inplace.restype = ctypes.c_int
         L.qkvnr_strerror.argtypes = [ctypes.c_int]
         L.qkvnr_strerror.restype = ctypes.c_char_p
         L.qkvnr_version.argtypes = []
@@ -160,6 +164,13 @@ def qkvnr_forward_paged(layout: Layout, qkv, positions, q_norm_w, k_norm_w, eps:
     _check(lib().qkvnr_forward_paged(ctypes.byref(layout), _ptr(qkv), _ptr(positions), _ptr(q_norm_w),
                                      _ptr(k_norm_w), eps, theta, _ptr(block_table), bt_stride, tokens_per_req,
                                      page_size, num_pages, _ptr(q), _ptr(k_pool), _ptr(v_pool), _stream(stream)))
+
+
+def qkvnr_rope_inplace(dtype: int, T: int, heads: int, token_stride: int, head_stride: int, rope_offset: int,
+                       rope_dim: int, positions, theta: float, x, stream=None) -> None:
+    """Call ``qkvnr_rope_inplace``."""
+    _check(lib().qkvnr_rope_inplace(dtype, T, heads, token_stride, head_stride, rope_offset, rope_dim,
+                                    _ptr(positions), theta, _ptr(x), _stream(stream)))
 
 
 def qkvnr_version() -> int:
@@ -262,3 +273,16 @@ def forward_latent_paged(rows: torch.Tensor, positions: torch.Tensor, norm_w: to
     L = latent_layout(rows, norm_dim, rope_dim)
     qkvnr_forward_paged(L, rows, positions, None, norm_w, eps, theta, block_table, block_table.shape[1],
                         tokens_per_req, pool.shape[1], pool.shape[0], None, pool, None, stream)
+
+
+def rope_inplace(x: torch.Tensor, positions: torch.Tensor, *, rope_offset: int, rope_dim: int = 64,
+                 theta: float = 10000.0, stream=None) -> torch.Tensor:
+    """Rotate x[..., rope_offset:rope_offset + rope_dim] in place; x is [T, heads, head_stride]
+    with a contiguous last dimension (token and head strides taken from the tensor)."""
+    if x.dim() != 3 or x.stride(2) != 1:
+        raise ValueError("x must be [T, heads, head_stride] with a contiguous last dimension")
+    if x.dtype not in DTYPES:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    qkvnr_rope_inplace(DTYPES[x.dtype], x.shape[0], x.shape[1], x.stride(0), x.stride(1), rope_offset, rope_dim,
+                       positions, theta, x, stream)
+    return x

@@ -516,4 +516,51 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_latent_kernel(const LatentA
   }
 }
 
+// ------------------------------------------------------------------ RoPE in place
+
+// The q path's rotation of each head's rope part ("rope_into" of the MLA
+// drafter layer): x [T, heads, head_stride] bf16, the R values at rope_off of
+// every head rotated in place at the token's position; nothing else is read
+// or written.  One wave per token; LPH = R/8 lanes per head in mirror chunk
+// order, HPI = 64/LPH heads per wave iteration.
+struct RopeArgs {
+  uint8_t* x;
+  int64_t T;
+  int64_t token_bytes;
+  int32_t head_bytes;
+  int32_t rope_off_bytes;
+  int32_t heads;
+  int32_t iters;  // ceil(heads / HPI)
+  const int32_t* pos;
+  double turns[kMaxPairs];
+};
+
+template <int R>
+__global__ __launch_bounds__(kBlockThreads) void rope_inplace_kernel(const RopeArgs a) {
+  constexpr int LPH = R / 8, HPI = kWave / LPH;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int li = lane & (LPH - 1);
+  const int hs = lane / LPH;
+  const int c = chunk_of_lane<LPH>(li);
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave;
+  if (t >= a.T) return;  // wave-uniform
+  const double tpp = a.turns[lane % (R / 2)];
+  const int32_t p = a.pos[t];
+  float cs[8], sn[8];
+  unit_cos_sin<8, LPH>(p, tpp, c, cs, sn);
+  uint8_t* base = a.x + t * a.token_bytes + a.rope_off_bytes + c * 16;
+  for (int it = 0; it < a.iters; ++it) {
+    const int h = it * HPI + hs;
+    if (h < a.heads) {  // the partner lane belongs to the same head, so it takes the same branch
+      uint8_t* ptr = base + static_cast<int64_t>(h) * a.head_bytes;
+      float k[8], z[8];
+      unpack(ld16(ptr), k);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) z[e] = fmaf(k[e], cs[e], partner<LPH>(k[e]) * sn[e]);
+      st16(ptr, pack(z));
+    }
+  }
+}
+
 }  // namespace qkvnr

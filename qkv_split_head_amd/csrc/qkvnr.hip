@@ -67,6 +67,13 @@ int launched(const char* what) {
 
 int elem_bytes(int32_t dtype) { return dtype == QKVNR_BF16 ? 2 : 4; }
 
+// Bytes a packed [T, in_row_stride] tensor's rows actually span: the last row
+// ends after `width` values, so a strided view of a wider buffer (padding or
+// other columns after it) is not counted past its own end.
+int64_t rows_extent(const qkvnr_layout* L, int es) {
+  return L->T == 0 ? 0 : ((L->T - 1) * L->in_row_stride + L->width) * es;
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
@@ -249,7 +256,7 @@ int latent_forward(const qkvnr_layout* L, const void* qkv, const int32_t* positi
   if (int rc = need16(k_norm_w, "k_norm_w (latent norm weight)")) return rc;
   if (int rc = need16(out, paged ? "k_pool" : "k")) return rc;
   const int64_t row_bytes = L->in_row_stride * 2;
-  if (int rc = check_disjoint({{out, out_bytes}}, {{qkv, L->T * row_bytes}, {positions, L->T * 4}, {k_norm_w, 1024}}))
+  if (int rc = check_disjoint({{out, out_bytes}}, {{qkv, rows_extent(L, 2)}, {positions, L->T * 4}, {k_norm_w, 1024}}))
     return rc;
   int cus = 0;
   if (int rc = current_device(&cus)) return rc;
@@ -295,7 +302,7 @@ int gqa_forward(const qkvnr_layout* L, const void* qkv, const int32_t* positions
   const int64_t D = L->head_dim, n_q = static_cast<int64_t>(L->n_kv) * L->q_per_kv;
   const int64_t wbytes = D * es;
   if (int rc = check_disjoint({{q, L->T * n_q * D * es}, {k, kv_bytes}, {v, kv_bytes}},
-                              {{qkv, L->T * L->in_row_stride * es},
+                              {{qkv, rows_extent(L, es)},
                                {positions, positions ? L->T * 4 : 0},
                                {q_norm_w, wbytes},
                                {k_norm_w, wbytes}}))
@@ -408,8 +415,8 @@ int qkvnr_backward(const qkvnr_layout* layout, const void* qkv, const int32_t* p
                 (long long)ws_need);
   const int64_t kvb = L->T * L->n_kv * D * es;
   if (int rc = check_disjoint(
-          {{dqkv, L->T * L->in_row_stride * es}, {dq_norm_w, D * 4}, {dk_norm_w, D * 4}, {workspace, ws_need}},
-          {{qkv, L->T * L->in_row_stride * es}, {positions, positions ? L->T * 4 : 0}, {q_norm_w, D * es},
+          {{dqkv, rows_extent(L, es)}, {dq_norm_w, D * 4}, {dk_norm_w, D * 4}, {workspace, ws_need}},
+          {{qkv, rows_extent(L, es)}, {positions, positions ? L->T * 4 : 0}, {q_norm_w, D * es},
            {k_norm_w, D * es}, {dq, L->T * n_q * D * es}, {dk, kvb}, {dv, kvb}}))
     return rc;
   if (int rc = current_device(&cus)) return rc;
@@ -434,6 +441,50 @@ int qkvnr_backward(const qkvnr_layout* layout, const void* qkv, const int32_t* p
   else
     hipLaunchKernelGGL(wgrad_fold_kernel<128>, dim3(1), dim3(kFoldThreads), 0, stream, a.slots, dq_norm_w, dk_norm_w);
   return launched("weight-grad fold");
+}
+
+int qkvnr_rope_inplace(int32_t dtype, int64_t T, int32_t heads, int64_t token_stride, int32_t head_stride,
+                       int32_t rope_offset, int32_t rope_dim, const int32_t* positions, double theta, void* x,
+                       hipStream_t stream) {
+  if (dtype != QKVNR_BF16 && dtype != QKVNR_FP32) return fail(QKVNR_EINVAL, "unknown dtype %d", dtype);
+  if (dtype != QKVNR_BF16) return fail(QKVNR_EUNSUPPORTED, "rope_inplace: only bf16 has a kernel");
+  if (T < 0 || T > INT32_MAX) return fail(QKVNR_EINVAL, "T = %lld out of [0, 2^31)", (long long)T);
+  if (heads < 1) return fail(QKVNR_EINVAL, "heads %d must be >= 1", heads);
+  if (rope_dim != 64 && rope_dim != 128)
+    return fail(QKVNR_EUNSUPPORTED, "rope_inplace: rope_dim %d: kernels exist for 64 and 128", rope_dim);
+  if (rope_offset < 0 || head_stride < 1 || static_cast<int64_t>(rope_offset) + rope_dim > head_stride)
+    return fail(QKVNR_EINVAL, "rope part [%d, %d) does not fit a head of stride %d", rope_offset,
+                rope_offset + rope_dim, head_stride);
+  if (static_cast<int64_t>(heads) * head_stride > token_stride)
+    return fail(QKVNR_EINVAL, "%d heads of stride %d do not fit a token stride of %lld", heads, head_stride,
+                (long long)token_stride);
+  if ((rope_offset * 2) % 16 || (head_stride * 2) % 16 || (token_stride * 2) % 16)
+    return fail(QKVNR_EALIGN, "rope offset, head stride and token stride must be multiples of 8 values");
+  if (!std::isfinite(theta) || theta <= 0.0) return fail(QKVNR_EINVAL, "theta %g must be finite and > 0", theta);
+  if (T == 0) return QKVNR_OK;  // nothing is read or written
+  if (int rc = need16(x, "x")) return rc;
+  if (int rc = need4(positions, "positions")) return rc;
+  const int64_t x_bytes = (T - 1) * token_stride * 2 + static_cast<int64_t>(heads) * head_stride * 2;
+  if (overlaps({x, x_bytes}, {positions, T * 4})) return fail(QKVNR_EINVAL, "x overlaps positions");
+  int cus = 0;
+  if (int rc = current_device(&cus)) return rc;
+  RopeArgs a{};
+  a.x = static_cast<uint8_t*>(x);
+  a.T = T;
+  a.token_bytes = token_stride * 2;
+  a.head_bytes = head_stride * 2;
+  a.rope_off_bytes = rope_offset * 2;
+  a.heads = heads;
+  const int hpi = kWave / (rope_dim / 8);
+  a.iters = (heads + hpi - 1) / hpi;
+  a.pos = positions;
+  fill_turns(a.turns, theta, rope_dim);
+  const dim3 g(static_cast<uint32_t>((T + kWavesPerBlock - 1) / kWavesPerBlock)), b(kBlockThreads);
+  if (rope_dim == 64)
+    hipLaunchKernelGGL(rope_inplace_kernel<64>, g, b, 0, stream, a);
+  else
+    hipLaunchKernelGGL(rope_inplace_kernel<128>, g, b, 0, stream, a);
+  return launched("rope in place");
 }
 
 const char* qkvnr_strerror(int code) {

@@ -54,20 +54,32 @@ def ulp_bf16(x: np.ndarray) -> np.ndarray:
     return np.exp2(np.floor(np.log2(x)) - 7)
 
 
-def assert_close(gpu_bits: np.ndarray, ref64: np.ndarray, dtype: str, what: str, scale=None) -> None:
+def assert_close(gpu_bits: np.ndarray, ref64: np.ndarray, dtype: str, what: str, scale=None,
+                 ulps: float = 2.0) -> None:
     """Element-wise tolerance check of stored GPU results against the fp64 oracle (rules above).
 
     ``gpu_bits`` are stored values (bf16 bit patterns or fp32); ``scale`` is the
     magnitude the floor is taken from: the rms of ``ref64`` by default.
     """
-    assert_values_close(host_value(gpu_bits, dtype), ref64, dtype, what, scale)
+    assert_values_close(host_value(gpu_bits, dtype), ref64, dtype, what, scale, ulps)
 
 
-def assert_values_close(got: np.ndarray, ref64: np.ndarray, rule: str, what: str, scale=None) -> None:
+def max_ulps_bf16(got: np.ndarray, ref64: np.ndarray) -> float:
+    """Largest |got - ref| in bf16 ulps of max(|ref|, 2**-8 * rms(ref)) (a report, not a check)."""
+    ref = np.asarray(ref64, dtype=np.float64)
+    got = np.asarray(got, dtype=np.float64).reshape(ref.shape)
+    floor = 2.0 ** -8 * np.sqrt(np.mean(ref * ref))
+    return float(np.max(np.abs(got - ref) / ulp_bf16(np.maximum(np.maximum(np.abs(ref), floor), 1e-30))))
+
+
+def assert_values_close(got: np.ndarray, ref64: np.ndarray, rule: str, what: str, scale=None,
+                        ulps: float = 2.0) -> None:
     """Tolerance check of GPU values (already decoded) under the ``rule`` of a dtype.
 
     Used directly for the fp32 norm-weight grads, which follow the rule of the
-    activation dtype with the floor taken from ``scale`` (per element).
+    activation dtype with the floor taken from ``scale`` (per element).  ``ulps``
+    widens the bf16 rule where a documented chain of library roundings precedes
+    the compared value (the MLA drafter layer); it is 2 everywhere else.
     """
     ref = np.asarray(ref64, dtype=np.float64)
     got = np.asarray(got, dtype=np.float64).reshape(ref.shape)
@@ -76,7 +88,7 @@ def assert_values_close(got: np.ndarray, ref64: np.ndarray, rule: str, what: str
     if scale is None:
         scale = np.sqrt(np.mean(ref * ref))
     if rule == "bf16":
-        tol = 2.0 * ulp_bf16(np.maximum(np.maximum(np.abs(ref), 2.0 ** -8 * np.asarray(scale)), 1e-30))
+        tol = ulps * ulp_bf16(np.maximum(np.maximum(np.abs(ref), 2.0 ** -8 * np.asarray(scale)), 1e-30))
     else:
         tol = 1e-5 * np.maximum(np.abs(ref), np.asarray(scale))
     tol = np.broadcast_to(tol, ref.shape)

@@ -176,12 +176,55 @@ def test_backward_workspace_size():
     assert qk.lib().qkvnr_backward_workspace_bytes(None) == cap
 
 
+def test_rope_inplace_argument_checks():
+    f = qk.lib().qkvnr_rope_inplace
+    # dtype, T, heads, token_stride, head_stride, rope_offset, rope_dim, positions, theta, x
+    ok = [qk.BF16, 16, 16, 16 * 192, 192, 128, 64, B, 1e4, A]
+
+    def call(**change):
+        a = list(ok)
+        for i, v in change.items():
+            a[int(i[1:])] = v
+        return f(*a, None)
+
+    assert call(i0=7) == qk.EINVAL                       # unknown dtype
+    assert call(i0=qk.FP32) == qk.EUNSUPPORTED           # fp32 has no kernel
+    assert call(i1=-1) == qk.EINVAL                      # T < 0
+    assert call(i2=0) == qk.EINVAL                       # no heads
+    assert call(i6=32) == qk.EUNSUPPORTED                # rope_dim without a kernel
+    assert call(i5=160) == qk.EINVAL                     # rope part past the head
+    assert call(i3=15 * 192) == qk.EINVAL                # heads do not fit the token stride
+    assert call(i5=124) == qk.EALIGN                     # rope offset not a multiple of 8 values
+    assert call(i4=196, i3=16 * 196) == qk.EALIGN        # head stride not a multiple of 8 values
+    assert call(i8=0.0) == qk.EINVAL                     # theta
+    assert call(i9=0) == qk.EINVAL                       # x NULL
+    assert call(i9=A + 2) == qk.EALIGN                   # x misaligned
+    assert call(i7=0) == qk.EINVAL                       # positions NULL
+    assert call(i7=A + 64) == qk.EINVAL                  # positions inside x
+    assert call(i1=0, i7=0, i9=0) == qk.OK               # empty batch: nothing is touched
+
+
 @pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU driver is present; this case is for GPU-less hosts")
 def test_valid_call_without_gpu_is_unsupported_not_a_crash():
     # every argument valid: the library reaches its device query, finds no gfx950, and says so
     assert _fwd(_lay()) == qk.EUNSUPPORTED
     assert "gfx950" in qk.lib().qkvnr_strerror(qk.EUNSUPPORTED).decode() or \
         "device" in qk.lib().qkvnr_strerror(qk.EUNSUPPORTED).decode()
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU driver is present; this case is for GPU-less hosts")
+def test_strided_rows_are_counted_to_their_last_value():
+    # latent rows as the last 576 columns of [T, 2112] rows (a merged projection's
+    # output): an output that starts right after the last row's last value does
+    # not overlap the input, although it lies within T * row_stride of its start
+    T, stride = 4, 2112
+    L = Layout(kind=qk.LATENT, dtype=qk.BF16, T=T, n_kv=1, q_per_kv=0, head_dim=0, rope_dim=64, norm_dim=512,
+               reserved=0, width=576, in_row_stride=stride)
+    rows = A + 1536 * 2
+    end = rows + ((T - 1) * stride + 576) * 2
+    f = qk.lib().qkvnr_forward
+    assert f(ctypes.byref(L), rows, B, None, C, 1e-6, 1e4, None, end, None, None) == qk.EUNSUPPORTED  # no GPU here
+    assert f(ctypes.byref(L), rows, B, None, C, 1e-6, 1e4, None, end - 16, None, None) == qk.EINVAL
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

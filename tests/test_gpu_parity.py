@@ -442,6 +442,39 @@ def test_mla_latent_paged_store_full_pool():
     assert_close(got[:, 512:], ref[:, 512:], "bf16", "pool rotated part")
 
 
+@pytest.mark.parametrize("T,heads,head_stride,rope_offset,rope_dim,token_pad", [
+    (16, 16, 192, 128, 64, 0),      # the MLA drafter's q heads: [nope 128 | rope 64]
+    (64, 16, 192, 128, 64, 0),
+    (37, 5, 136, 8, 128, 24),       # ragged heads per wave, rope part in the middle, padded token stride
+    (1, 1, 64, 0, 64, 0),
+    (300, 9, 72, 8, 64, 8),
+])
+def test_rope_inplace_matches_oracle(T, heads, head_stride, rope_offset, rope_dim, token_pad):
+    rng = np.random.default_rng(T * 7 + heads)
+    from qkv_inputs import bf16_bits_from_f32
+    token_stride = heads * head_stride + token_pad
+    bits = bf16_bits_from_f32(rng.standard_normal((T, token_stride)).astype(np.float32))
+    pos = rng.integers(0, 131072, size=T).astype(np.int32)
+    x = to_dev(bits, "bf16")
+    view = x.view(T, token_stride)[:, :heads * head_stride].view(T, heads, head_stride)
+    qk.rope_inplace(view, to_dev(pos, "int32"), rope_offset=rope_offset, rope_dim=rope_dim, theta=1e4)
+    got = to_host_bits(x)
+    torch.cuda.synchronize()
+    heads_h = bits[:, :heads * head_stride].reshape(T, heads, head_stride)
+    got_h = got[:, :heads * head_stride].reshape(T, heads, head_stride)
+    part = slice(rope_offset, rope_offset + rope_dim)
+    ref = oracle.rope_rotate_half(oracle.to_f64(heads_h[..., part], "bf16"), oracle.rope_angles(pos, 1e4, rope_dim))
+    assert_close(got_h[..., part], ref, "bf16", "rope part")
+    keep = np.ones(head_stride, bool)
+    keep[part] = False
+    assert_bits_equal(got_h[..., keep], heads_h[..., keep], "rest of each head")
+    assert_bits_equal(got[:, heads * head_stride:], bits[:, heads * head_stride:], "token padding")
+
+
+def test_rope_inplace_empty_batch_is_a_no_op():
+    qk.qkvnr_rope_inplace(qk.BF16, 0, 4, 4 * 64, 64, 0, 64, None, 1e4, None)
+
+
 # ------------------------------------------------------------------ full-size workloads (sampled)
 
 

@@ -1,6 +1,7 @@
 """The oracle's pins catch plausible mistakes (CPU only).
 
-Each case plants one mistake in a temporary copy of ``oracle/reference.py``
+Each case plants one mistake in a temporary copy of ``oracle/reference.py`` or
+``oracle/mla_drafter.py``
 (a dropped term, a wrong sign, a wrong index, a swapped operand) and runs the
 pin suite against that copy in a subprocess: the suite must fail.  Nothing
 here touches the GPU or the HIP library.
@@ -46,24 +47,42 @@ MUTANTS = {
 }
 
 
-def _run(name, old, new, tmp):
-    src = open(SRC).read()
+# mistakes in the MLA drafter layer oracle, caught by its own pin file
+DRAFTER_MUTANTS = {
+    "absorb_wrong_head": ('return np.einsum("nhd,hdl->nhl", q_nope, w_uk)',
+                          'return np.einsum("nhd,hdl->nhl", q_nope, w_uk[::-1])'),
+    "q_rope_not_applied": ("q_pe = _store(rope_rotate_half(q[..., qk_nope_head_dim:], "
+                           "rope_angles(pos, theta, qk_rope_head_dim)), storage)",
+                           "q_pe = _store(q[..., qk_nope_head_dim:], storage)"),
+    "q_nope_rope_parts_swapped": ("q_nope = q[..., :qk_nope_head_dim]", "q_nope = q[..., qk_rope_head_dim:]"),
+    "q_a_norm_dropped": ("q_a = _store(rmsnorm(q_a, to_f64(w_q_a_ln, dtype), eps), storage)", "q_a = q_a"),
+    "kv_from_unnormed_input": ("kv = _store(xn @ to_f64(w_kv_a, dtype), storage)",
+                               "kv = _store(X @ to_f64(w_kv_a, dtype), storage)"),
+    "storage_skipped": ('    if storage is None:\n        return x\n', '    return x\n'),
+}
+DRAFTER_SRC = os.path.join(ROOT, "oracle", "mla_drafter.py")
+
+
+def _run(name, old, new, tmp, src_path=SRC, pins="test_oracle_pins.py"):
+    src = open(src_path).read()
     assert src.count(old) == 1, f"{name}: anchor not found exactly once"
     d = os.path.join(tmp, name)
     shutil.copytree(os.path.join(ROOT, "oracle"), os.path.join(d, "oracle"),
                     ignore=shutil.ignore_patterns("__pycache__"))
-    with open(os.path.join(d, "oracle", "reference.py"), "w") as f:
+    with open(os.path.join(d, "oracle", os.path.basename(src_path)), "w") as f:
         f.write(src.replace(old, new))
     env = dict(os.environ, PYTHONPATH=d + os.pathsep + ROOT, PYTHONDONTWRITEBYTECODE="1")
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        os.path.join(ROOT, "tests", pins)],
                        cwd=d, env=env, capture_output=True, text=True, timeout=600)
     return name, r.returncode, (r.stdout.strip().splitlines() or [""])[-1]
 
 
 def test_every_planted_mistake_fails_a_pin(tmp_path):
+    jobs = [(n, o, w, SRC, "test_oracle_pins.py") for n, (o, w) in MUTANTS.items()]
+    jobs += [(n, o, w, DRAFTER_SRC, "test_oracle_mla_drafter.py") for n, (o, w) in DRAFTER_MUTANTS.items()]
     with ThreadPoolExecutor(max_workers=4) as ex:
-        results = list(ex.map(lambda kv: _run(kv[0], *kv[1], str(tmp_path)), MUTANTS.items()))
+        results = list(ex.map(lambda j: _run(j[0], j[1], j[2], str(tmp_path), j[3], j[4]), jobs))
     survivors = [(n, tail) for n, rc, tail in results if rc != 1]
     assert not survivors, f"mistakes no pin caught (or the run broke): {survivors}"
 
@@ -71,6 +90,9 @@ def test_every_planted_mistake_fails_a_pin(tmp_path):
 def test_unmutated_copy_passes(tmp_path):
     # the harness itself: the same run on an unchanged copy must pass
     name, rc, tail = _run("unchanged", "def head_blocks(", "def head_blocks(", str(tmp_path))
+    assert rc == 0, tail
+    name, rc, tail = _run("unchanged_drafter", "def absorb(", "def absorb(", str(tmp_path), DRAFTER_SRC,
+                          "test_oracle_mla_drafter.py")
     assert rc == 0, tail
 
 
