@@ -178,10 +178,14 @@ __device__ __forceinline__ bool wave_unit(const GqaArgs& a, int U, int waves_per
 
 // ------------------------------------------------------------------ forward
 
-template <typename IO, int D, bool ROPE, bool PAGED>
+// U iterations per work unit, DEPTH of their loads in flight at once: (kFwdU,
+// kFwdDepth) for streaming batches, (1, 1) for small batches, where the
+// shortest per-wave chain (one load, one store) gives the lowest latency.
+template <typename IO, int D, bool ROPE, bool PAGED, int U, int DEPTH>
 __global__ __launch_bounds__(kBlockThreads) void fwd_gqa_kernel(const GqaArgs a) {
+  static_assert(DEPTH >= 1 && DEPTH <= U, "load depth must be in [1, units]");
   using G = Geo<IO, D>;
-  constexpr int EPC = G::EPC, LPH = G::LPH, HPI = G::HPI, HB = G::HB, U = kFwdU;
+  constexpr int EPC = G::EPC, LPH = G::LPH, HPI = G::HPI, HB = G::HB;
   const int lane = threadIdx.x & (kWave - 1);
   const int li = lane & (LPH - 1);
   const int hs = lane / LPH;
@@ -207,11 +211,11 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_gqa_kernel(const GqaArgs a)
 
   // Streaming loads without branches: a lane past the last head re-reads the
   // last head block (same row, already in flight), and its result is dropped.
-  // kFwdDepth of them go out at once; each store is followed by the next load.
+  // DEPTH of them go out at once; each store is followed by the next load.
   const uint8_t* row = a.qkv + t * a.row_bytes;
   uint4 buf[U];
 #pragma unroll
-  for (int j = 0; j < kFwdDepth; ++j)
+  for (int j = 0; j < DEPTH; ++j)
     buf[j] = ld_stream(row + min((it0 + j) * HPI + hs, a.heads - 1) * HB + cb);
   __builtin_amdgcn_sched_barrier(0);
 
@@ -246,9 +250,9 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_gqa_kernel(const GqaArgs a)
     uint8_t* dst = type == 0 ? a.q + (t * a.n_q + idx) * HB
                              : (type == 1 ? a.k : a.v) + (kv_tok * a.n_kv + idx) * HB;
     if (h < a.heads && (type == 0 || kv_tok >= 0)) st_stream(dst + cb, out);
-    if (j + kFwdDepth < U) {
+    if (j + DEPTH < U) {
       __builtin_amdgcn_sched_barrier(0);
-      buf[j + kFwdDepth] = ld_stream(row + min((it0 + j + kFwdDepth) * HPI + hs, a.heads - 1) * HB + cb);
+      buf[j + DEPTH] = ld_stream(row + min((it0 + j + DEPTH) * HPI + hs, a.heads - 1) * HB + cb);
       __builtin_amdgcn_sched_barrier(0);
     }
   }

@@ -218,10 +218,15 @@ int unit_grid(const GqaArgs& a, int waves_per_block) {
   return static_cast<int>((a.units + waves_per_block - 1) / waves_per_block);
 }
 
-template <bool PAGED>
+// Below this many work units of kFwdU iterations (8 waves per CU of the
+// part), a batch is latency-bound: the forward then uses one iteration per wave.
+constexpr int64_t kSmallBatchUnits = 2048;
+
+template <bool PAGED, int U, int DEPTH>
 void launch_fwd_gqa(const GqaArgs& a, int32_t dtype, int32_t D, bool rope, hipStream_t s) {
   const dim3 g(unit_grid(a, kWavesPerBlock)), b(kBlockThreads);
-#define QKVNR_FWD(IO, DD, R) hipLaunchKernelGGL((fwd_gqa_kernel<IO, DD, R, PAGED>), g, b, QKVNR_FWD_LDS, s, a)
+#define QKVNR_FWD(IO, DD, R) \
+  hipLaunchKernelGGL((fwd_gqa_kernel<IO, DD, R, PAGED, U, DEPTH>), g, b, QKVNR_FWD_LDS, s, a)
   if (dtype == QKVNR_BF16) {
     if (D == 64) { if (rope) QKVNR_FWD(uint16_t, 64, true); else QKVNR_FWD(uint16_t, 64, false); }
     else         { if (rope) QKVNR_FWD(uint16_t, 128, true); else QKVNR_FWD(uint16_t, 128, false); }
@@ -311,6 +316,8 @@ int gqa_forward(const qkvnr_layout* L, const void* qkv, const int32_t* positions
   if (int rc = current_device(&cus)) return rc;
   GqaArgs a{};
   plan_gqa(a, L, kFwdU, theta);
+  const bool small = a.units < kSmallBatchUnits;
+  if (small) plan_gqa(a, L, 1, theta);
   a.qkv = static_cast<const uint8_t*>(qkv);
   a.pos = positions;
   a.wq = static_cast<const uint8_t*>(q_norm_w);
@@ -324,10 +331,13 @@ int gqa_forward(const qkvnr_layout* L, const void* qkv, const int32_t* positions
   a.tokens_per_req = tokens_per_req;
   a.page_size = page_size;
   a.num_pages = num_pages;
-  if (paged)
-    launch_fwd_gqa<true>(a, L->dtype, L->head_dim, rope, stream);
-  else
-    launch_fwd_gqa<false>(a, L->dtype, L->head_dim, rope, stream);
+  if (paged) {
+    if (small) launch_fwd_gqa<true, 1, 1>(a, L->dtype, L->head_dim, rope, stream);
+    else launch_fwd_gqa<true, kFwdU, kFwdDepth>(a, L->dtype, L->head_dim, rope, stream);
+  } else {
+    if (small) launch_fwd_gqa<false, 1, 1>(a, L->dtype, L->head_dim, rope, stream);
+    else launch_fwd_gqa<false, kFwdU, kFwdDepth>(a, L->dtype, L->head_dim, rope, stream);
+  }
   return launched("forward");
 }
 

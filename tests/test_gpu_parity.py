@@ -142,7 +142,28 @@ FWD_CASES = [
     ("sectioned", "bf16", 100, 4, 2, 64, False, "random"),     # NoPE
     ("interleaved", "fp32", 50, 2, 2, 64, False, "random"),    # NoPE fp32
     ("interleaved", "bf16", 5000, 4, 4, 64, True, "arange"),   # many units per wave
+    # enough work units for the streaming schedule (4 iterations per wave, 3 loads in flight);
+    # the cases above with fewer units take the one-iteration-per-wave schedule
+    ("interleaved", "bf16", 3000, 3, 5, 64, True, "random"),   # 21 heads: ragged last iteration
+    ("sectioned", "bf16", 2100, 8, 4, 128, True, "random"),    # 12 iterations: 3 full units per token
+    ("interleaved", "fp32", 2500, 2, 3, 128, True, "random"),  # 5 iterations: a unit of 4 and a unit of 1
+    ("sectioned", "bf16", 2200, 2, 5, 64, True, "random"),     # 2 iterations in a unit of 4
+    ("interleaved", "bf16", 4096, 16, 8, 64, False, "random"), # NoPE
 ]
+
+
+@pytest.mark.parametrize("kind,dtype,n_kv,Q,D", [("interleaved", "bf16", 16, 8, 64), ("sectioned", "bf16", 8, 4, 128),
+                                                  ("interleaved", "fp32", 3, 2, 128)])
+def test_small_and_streaming_schedules_agree_bitwise(kind, dtype, n_kv, Q, D):
+    # the same tokens through the streaming schedule (a large batch) and the
+    # one-iteration schedule (a small prefix of it): bitwise the same outputs
+    w = custom_gqa(kind, dtype, 12000, n_kv, Q, D, theta=1e4, seed=31, positions="random")
+    big = _gpu_forward(w)
+    n = 40
+    w.qkv, w.positions, w.T = w.qkv[:n], w.positions[:n], n
+    small = _gpu_forward(w)
+    for a, b, name in zip(big, small, "qkv"):
+        assert_bits_equal(a[:n], b, f"{name}: streaming vs small-batch schedule")
 
 
 @pytest.mark.parametrize("case", FWD_CASES, ids=lambda c: "-".join(map(str, c)))
