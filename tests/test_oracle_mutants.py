@@ -1,7 +1,7 @@
 """The oracle's pins catch plausible mistakes (CPU only).
 
-Each case plants one mistake in a temporary copy of ``oracle/reference.py`` or
-``oracle/mla_drafter.py``
+Each case plants one mistake in a temporary copy of ``oracle/reference.py``,
+``oracle/mla_drafter.py`` or ``oracle/muon.py``
 (a dropped term, a wrong sign, a wrong index, a swapped operand) and runs the
 pin suite against that copy in a subprocess: the suite must fail.  Nothing
 here touches the GPU or the HIP library.
@@ -62,6 +62,16 @@ DRAFTER_MUTANTS = {
 }
 DRAFTER_SRC = os.path.join(ROOT, "oracle", "mla_drafter.py")
 
+# mistakes in the per-head Newton-Schulz oracle, caught by its own pin file
+MUON_MUTANTS = {
+    "ns_coefficient_sign": ("X = a * X + (b * A + c * (A @ A)) @ X", "X = a * X + (b * A - c * (A @ A)) @ X"),
+    "ns_polynomial_on_the_right": ("X = a * X + (b * A + c * (A @ A)) @ X", "X = a * X + X @ (b * A + c * (A @ A))"),
+    "ns_spectral_normalisation": ("X = X / (np.sqrt(np.sum(X * X)) + eps)", "X = X / (np.linalg.norm(X, 2) + eps)"),
+    "scale_inverted": ("return max(1.0, rows / cols) ** 0.5", "return max(1.0, cols / rows) ** 0.5"),
+    "blocks_without_v": ("blocks = n_q + 2 * n_kv", "blocks = n_q + n_kv"),
+}
+MUON_SRC = os.path.join(ROOT, "oracle", "muon.py")
+
 
 def _run(name, old, new, tmp, src_path=SRC, pins="test_oracle_pins.py"):
     src = open(src_path).read()
@@ -81,6 +91,7 @@ def _run(name, old, new, tmp, src_path=SRC, pins="test_oracle_pins.py"):
 def test_every_planted_mistake_fails_a_pin(tmp_path):
     jobs = [(n, o, w, SRC, "test_oracle_pins.py") for n, (o, w) in MUTANTS.items()]
     jobs += [(n, o, w, DRAFTER_SRC, "test_oracle_mla_drafter.py") for n, (o, w) in DRAFTER_MUTANTS.items()]
+    jobs += [(n, o, w, MUON_SRC, "test_oracle_muon.py") for n, (o, w) in MUON_MUTANTS.items()]
     with ThreadPoolExecutor(max_workers=4) as ex:
         results = list(ex.map(lambda j: _run(j[0], j[1], j[2], str(tmp_path), j[3], j[4]), jobs))
     survivors = [(n, tail) for n, rc, tail in results if rc != 1]
