@@ -162,6 +162,48 @@ def drafter_extras(dev_bf16, stream, layers_n: int = 4, n: int = 30):
     return out
 
 
+def muon_extras(stream, n: int = 10):
+    """One Muon orthogonalisation (5 quintic Newton-Schulz steps) of the Qwen3-8B-like fused
+    q|k|v weight [6144, 4096] (seeded N(0,1)): per head (48 blocks of 128 rows) in bf16 and
+    fp32, and on the whole matrix in bf16 (the full-matrix path, library products only)."""
+    import torch
+    from qkv_split_head_amd.muon import per_head_newton_schulz
+
+    g = torch.Generator(device="cuda").manual_seed(80)
+    G = torch.randn((6144, 4096), generator=g, device="cuda").to(torch.bfloat16)
+    a, b_, c = 3.4445, -4.7750, 2.0315
+
+    def full_matrix():
+        X = G.t().contiguous()                    # wide orientation [4096, 6144]
+        X = X / (X.float().norm() + 1e-7).to(X.dtype)
+        for _ in range(5):
+            A = X @ X.t().contiguous()
+            X = a * X + (b_ * A + c * (A @ A)) @ X
+        return X.t() * (6144 / 4096) ** 0.5
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return round(e0.elapsed_time(e1) / n * 1e3, 1)
+
+    out = {
+        "weight": [6144, 4096], "head_blocks": 48, "steps": 5,
+        "per_head_bf16_us": timed(lambda: per_head_newton_schulz(G, 32, 8, 128)),
+        "per_head_fp32_us": timed(lambda: per_head_newton_schulz(G, 32, 8, 128, compute_dtype=torch.float32)),
+        "full_matrix_bf16_us": timed(full_matrix),
+    }
+    # products per step: Gram (2 d^2 cols per block) and update (2 d^2 cols), d = 128, cols = 4096
+    out["per_head_TFLOPs_bf16"] = round(5 * 48 * 4 * 128 * 128 * 4096 / (out["per_head_bf16_us"] * 1e-6) / 1e12, 1)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -362,6 +404,9 @@ def main():
 
         # ------------------------------------------------------------ MLA drafter layers: kv path beside q path
         extras["mla_drafter"] = drafter_extras(dev_bf16, stream)
+
+        # ------------------------------------------------------------ per-head Newton-Schulz on the fused weight
+        extras["muon_newton_schulz"] = muon_extras(stream)
 
     out = {
         "metric": METRIC,

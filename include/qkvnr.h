@@ -229,6 +229,64 @@ int qkvnr_rope_inplace(int32_t dtype, int64_t T, int32_t heads, int64_t token_st
                        int32_t head_stride, int32_t rope_offset, int32_t rope_dim,
                        const int32_t* positions, double theta, void* x, hipStream_t stream);
 
+/*
+ * Per-head Newton-Schulz on fused QKV weights (DeepSpeed page "[muon]
+ * Per-head Newton-Schulz for fused QKV projections", "What this PR does" and
+ * "Not in this PR").
+ *
+ * qkvnr_fused_head_blocks: the exact-total guard.  A fused q|k|v weight is
+ * split into head blocks of head_dim rows only when its row count is exactly
+ * (n_q + 2 n_kv) * head_dim; then *blocks = n_q + 2 n_kv (12 for 8 query heads
+ * over 2 kv heads) and QKVNR_OK.  Any other row count (a transposed Conv1D
+ * weight, a config whose fused total does not describe the weight) is
+ * QKVNR_EINVAL with *blocks = 0: such a weight stays on the full-matrix path.
+ * The guard is the same for the sectioned and the interleaved order, whose
+ * blocks differ only in order.  Host only: no HIP call.
+ */
+int qkvnr_fused_head_blocks(int32_t n_q, int32_t n_kv, int32_t head_dim, int64_t weight_rows,
+                            int64_t* blocks);
+
+/*
+ * Gram matrices X X^T of bf16 blocks, as partial sums over column slices:
+ * the first product of each Newton-Schulz step (and G G^T for the first).
+ * Both factors are rows of X, read along the long side; v_mfma_f32_32x32x16_bf16.
+ *
+ *   blocks  number of blocks, >= 0 (0 is a no-op).
+ *   d       block side (rows of each block): 32, 64, 96 or 128 (others
+ *           QKVNR_EUNSUPPORTED).
+ *   cols    block width, a positive multiple of 8 (QKVNR_EALIGN otherwise).
+ *   x       [blocks, d, cols] bf16, row-major, 16-byte aligned.
+ *   parts   column slices, 1..65535: slice p covers columns
+ *           [p * S, min(cols, (p + 1) * S)), S = ceil(ceil(cols / parts) / 16) * 16.
+ *   out     [blocks, parts, d, d] fp32, 4-byte aligned, must not overlap x;
+ *           out[b][p] is block b's Gram matrix over slice p (zero for an empty slice).
+ */
+int qkvnr_gram_partials(int64_t blocks, int32_t d, int64_t cols, const void* x, int32_t parts,
+                        float* out, hipStream_t stream);
+
+/*
+ * One Newton-Schulz step's polynomial for every block: from A (the Gram matrix
+ * X X^T of the block's wide orientation, d x d, given as `parts` partial sums
+ * that are added), P = a I + b A + c A A with Muon's quintic coefficients
+ * (a, b, c) = (3.4445, -4.7750, 2.0315); the step itself is X <- P X.  With
+ * first != 0, A is G G^T of the unnormalised block: it is divided by
+ * (||G||_F + eps)^2 (the norm is the square root of its trace) and P by
+ * (||G||_F + eps), so that P G is the first step from G / (||G||_F + eps).  P is
+ * multiplied by `scale` (pass the block scale max(1, rows/cols)**0.5 on the
+ * last step, 1 otherwise).  The update P X is the caller's batched GEMM.
+ *
+ *   dtype   QKVNR_BF16 or QKVNR_FP32: the type of p.
+ *   blocks  number of blocks, >= 0 (0 is a no-op).
+ *   d       block side, 1..128 (others QKVNR_EUNSUPPORTED).
+ *   gram    [blocks, parts, d, d] fp32, row-major, 16-byte aligned.  With
+ *           parts > 1 it is also written: each block's partial 0 becomes the
+ *           sum of its partials (the others are left as they were).
+ *   parts   >= 1.
+ *   p       out [blocks, d, d] in dtype, row-major; must not overlap gram.
+ */
+int qkvnr_ns_poly(int32_t dtype, int64_t blocks, int32_t d, float* gram, int32_t parts,
+                  int32_t first, float scale, float eps, void* p, hipStream_t stream);
+
 /* Static text for a return code.  For QKVNR_EHIP and the validation errors it
  * returns the last detailed message recorded on the calling thread. */
 const char* qkvnr_strerror(int code);

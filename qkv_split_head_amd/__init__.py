@@ -6,7 +6,8 @@ named like the C entry points (``qkvnr_forward``, ``qkvnr_backward``,
 ``backward``, ``forward_paged``, ``forward_latent`` and
 ``forward_latent_paged`` also allocate the outputs; ``rope_inplace`` rotates a
 tensor's rope parts in place.  ``mla_drafter`` runs an MLA drafter layer's kv
-path beside its q path on two streams.
+path beside its q path on two streams; ``muon`` runs per-head Newton-Schulz
+on fused QKV weights.
 """
 from ._binding import (  # noqa: F401
     BF16,
@@ -35,6 +36,9 @@ from ._binding import (  # noqa: F401
     qkvnr_backward_workspace_bytes,
     qkvnr_forward,
     qkvnr_forward_paged,
+    qkvnr_fused_head_blocks,
+    qkvnr_gram_partials,
+    qkvnr_ns_poly,
     qkvnr_rope_inplace,
     rope_inplace,
     qkvnr_version,

@@ -79,6 +79,15 @@ def lib() -> ctypes.CDLL:
                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, i32p, ctypes.c_double,
                                          vp, vp]
         L.qkvnr_rope_inplace.restype = ctypes.c_int
+        L.qkvnr_fused_head_blocks.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                              ctypes.POINTER(ctypes.c_int64)]
+        L.qkvnr_fused_head_blocks.restype = ctypes.c_int
+        L.qkvnr_gram_partials.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int64, vp, ctypes.c_int32,
+                                          vp, vp]
+        L.qkvnr_gram_partials.restype = ctypes.c_int
+        L.qkvnr_ns_poly.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, vp, ctypes.c_int32,
+                                    ctypes.c_int32, ctypes.c_float, ctypes.c_float, vp, vp]
+        L.qkvnr_ns_poly.restype = ctypes.c_int
         L.qkvnr_strerror.argtypes = [ctypes.c_int]
         L.qkvnr_strerror.restype = ctypes.c_char_p
         L.qkvnr_version.argtypes = []
@@ -171,6 +180,25 @@ def qkvnr_rope_inplace(dtype: int, T: int, heads: int, token_stride: int, head_s
     """Call ``qkvnr_rope_inplace``."""
     _check(lib().qkvnr_rope_inplace(dtype, T, heads, token_stride, head_stride, rope_offset, rope_dim,
                                     _ptr(positions), theta, _ptr(x), _stream(stream)))
+
+
+def qkvnr_fused_head_blocks(n_q: int, n_kv: int, head_dim: int, weight_rows: int) -> int:
+    """Head blocks of a fused q|k|v weight (the exact-total guard); raises QkvnrError when declined."""
+    out = ctypes.c_int64(0)
+    _check(lib().qkvnr_fused_head_blocks(n_q, n_kv, head_dim, weight_rows, ctypes.byref(out)))
+    return out.value
+
+
+def qkvnr_gram_partials(blocks: int, d: int, cols: int, x, parts: int, out, stream=None) -> None:
+    """Call ``qkvnr_gram_partials``."""
+    _check(lib().qkvnr_gram_partials(blocks, d, cols, _ptr(x), parts, _ptr(out), _stream(stream)))
+
+
+def qkvnr_ns_poly(dtype: int, blocks: int, d: int, gram, parts: int, first: bool, scale: float, eps: float, p,
+                  stream=None) -> None:
+    """Call ``qkvnr_ns_poly``."""
+    _check(lib().qkvnr_ns_poly(dtype, blocks, d, _ptr(gram), parts, 1 if first else 0, scale, eps, _ptr(p),
+                               _stream(stream)))
 
 
 def qkvnr_version() -> int:

@@ -9,6 +9,7 @@
 #include <mutex>
 
 #include "kernels.h"
+#include "muon.h"
 #include "qkvnr.h"
 
 namespace {
@@ -495,6 +496,82 @@ int qkvnr_rope_inplace(int32_t dtype, int64_t T, int32_t heads, int64_t token_st
   else
     hipLaunchKernelGGL(rope_inplace_kernel<128>, g, b, 0, stream, a);
   return launched("rope in place");
+}
+
+int qkvnr_fused_head_blocks(int32_t n_q, int32_t n_kv, int32_t head_dim, int64_t weight_rows, int64_t* blocks) {
+  if (!blocks) return fail(QKVNR_EINVAL, "blocks is NULL");
+  *blocks = 0;
+  if (n_q < 0 || n_kv < 0 || n_q + static_cast<int64_t>(n_kv) < 1 || head_dim < 1)
+    return fail(QKVNR_EINVAL, "n_q %d, n_kv %d, head_dim %d do not describe heads", n_q, n_kv, head_dim);
+  const int64_t heads = n_q + 2 * static_cast<int64_t>(n_kv);
+  if (weight_rows != heads * head_dim)
+    return fail(QKVNR_EINVAL, "weight of %lld rows is not the exact fused total (n_q + 2 n_kv) * head_dim = %lld",
+                (long long)weight_rows, (long long)(heads * head_dim));
+  *blocks = heads;
+  return QKVNR_OK;
+}
+
+int qkvnr_gram_partials(int64_t blocks, int32_t d, int64_t cols, const void* x, int32_t parts, float* out,
+                        hipStream_t stream) {
+  if (blocks < 0 || blocks > INT32_MAX) return fail(QKVNR_EINVAL, "blocks %lld out of [0, 2^31)", (long long)blocks);
+  if (d != 32 && d != 64 && d != 96 && d != 128)
+    return fail(QKVNR_EUNSUPPORTED, "block side %d: kernels exist for 32, 64, 96 and 128", d);
+  if (cols < 1 || cols % 8) return fail(QKVNR_EALIGN, "cols %lld must be a positive multiple of 8", (long long)cols);
+  if (parts < 1 || parts > 65535) return fail(QKVNR_EINVAL, "parts %d out of [1, 65535]", parts);
+  if (blocks == 0) return QKVNR_OK;
+  if (int rc = need16(x, "x")) return rc;
+  if (int rc = need4(out, "out")) return rc;
+  const int64_t n_out = blocks * parts * d * d;
+  if (overlaps({x, blocks * d * cols * 2}, {out, n_out * 4})) return fail(QKVNR_EINVAL, "out overlaps x");
+  int cus = 0;
+  if (int rc = current_device(&cus)) return rc;
+  // column slices of a multiple of 16, as even as that allows
+  const int64_t slice = ((cols + parts - 1) / parts + 15) / 16 * 16;
+  const dim3 g(static_cast<uint32_t>(blocks), static_cast<uint32_t>(parts));
+  const auto* xs = static_cast<const uint16_t*>(x);
+  switch (d) {
+    case 32: hipLaunchKernelGGL(gram_partials_kernel<32>, g, dim3(kWave * 1), 0, stream, xs, cols, slice, out); break;
+    case 64: hipLaunchKernelGGL(gram_partials_kernel<64>, g, dim3(kWave * 2), 0, stream, xs, cols, slice, out); break;
+    case 96: hipLaunchKernelGGL(gram_partials_kernel<96>, g, dim3(kWave * 3), 0, stream, xs, cols, slice, out); break;
+    default: hipLaunchKernelGGL(gram_partials_kernel<128>, g, dim3(kWave * 4), 0, stream, xs, cols, slice, out); break;
+  }
+  return launched("Gram partials");
+}
+
+int qkvnr_ns_poly(int32_t dtype, int64_t blocks, int32_t d, float* gram, int32_t parts, int32_t first,
+                  float scale, float eps, void* p, hipStream_t stream) {
+  if (dtype != QKVNR_BF16 && dtype != QKVNR_FP32) return fail(QKVNR_EINVAL, "unknown dtype %d", dtype);
+  if (blocks < 0 || blocks > INT32_MAX) return fail(QKVNR_EINVAL, "blocks %lld out of [0, 2^31)", (long long)blocks);
+  if (d < 1 || d > kNsMaxD) return fail(QKVNR_EUNSUPPORTED, "block side %d: the kernel holds 1..%d", d, kNsMaxD);
+  if (parts < 1) return fail(QKVNR_EINVAL, "parts %d must be >= 1", parts);
+  if (!std::isfinite(scale) || scale <= 0.0f) return fail(QKVNR_EINVAL, "scale %g must be finite and > 0", (double)scale);
+  if (!std::isfinite(eps) || eps < 0.0f) return fail(QKVNR_EINVAL, "eps %g must be finite and >= 0", (double)eps);
+  if (blocks == 0) return QKVNR_OK;
+  if (int rc = need16(gram, "gram")) return rc;
+  if (!p) return fail(QKVNR_EINVAL, "p is NULL");
+  if (reinterpret_cast<uintptr_t>(p) % elem_bytes(dtype)) return fail(QKVNR_EALIGN, "p is not aligned to its dtype");
+  const int64_t n = blocks * d * d;
+  if (overlaps({gram, n * parts * 4}, {p, n * elem_bytes(dtype)})) return fail(QKVNR_EINVAL, "p overlaps gram");
+  int cus = 0;
+  if (int rc = current_device(&cus)) return rc;
+  if (parts > 1) {  // the partials are summed into each block's partial 0
+    const int64_t total = blocks * d * d;
+    hipLaunchKernelGGL(gram_reduce_kernel, dim3(static_cast<uint32_t>((total + kNsThreads - 1) / kNsThreads)),
+                       dim3(kNsThreads), 0, stream, const_cast<float*>(gram), parts, d * d, total);
+    if (int rc = launched("Gram reduction")) return rc;
+  }
+  const dim3 grid(static_cast<uint32_t>(blocks), static_cast<uint32_t>((d + 31) / 32));
+  const int fi = first ? 1 : 0;
+  if (dtype == QKVNR_BF16) {
+    auto* o = static_cast<uint16_t*>(p);
+    if (d == 128) hipLaunchKernelGGL((ns_poly_kernel<uint16_t, 128>), grid, dim3(kNsThreads), 0, stream, gram, o, d, parts, fi, scale, eps);
+    else hipLaunchKernelGGL((ns_poly_kernel<uint16_t, 0>), grid, dim3(kNsThreads), 0, stream, gram, o, d, parts, fi, scale, eps);
+  } else {
+    auto* o = static_cast<float*>(p);
+    if (d == 128) hipLaunchKernelGGL((ns_poly_kernel<float, 128>), grid, dim3(kNsThreads), 0, stream, gram, o, d, parts, fi, scale, eps);
+    else hipLaunchKernelGGL((ns_poly_kernel<float, 0>), grid, dim3(kNsThreads), 0, stream, gram, o, d, parts, fi, scale, eps);
+  }
+  return launched("Newton-Schulz polynomial");
 }
 
 const char* qkvnr_strerror(int code) {

@@ -227,6 +227,72 @@ def test_strided_rows_are_counted_to_their_last_value():
     assert f(ctypes.byref(L), rows, B, None, C, 1e-6, 1e4, None, end - 16, None, None) == qk.EINVAL
 
 
+def test_fused_head_block_guard():
+    import json
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_layout_examples.json")))
+    hb = g["head_block_count"]
+    assert qk.qkvnr_fused_head_blocks(hb["n_q"], hb["n_kv"], 64, hb["blocks"] * 64) == hb["blocks"]
+    f = g["falcon_exact_total"]
+    assert qk.qkvnr_fused_head_blocks(8, 8, 8, f["config_rows"]) == 24
+    with pytest.raises(qk.QkvnrError):
+        qk.qkvnr_fused_head_blocks(8, 8, 8, f["weight_rows"])        # declined
+    with pytest.raises(qk.QkvnrError):
+        qk.qkvnr_fused_head_blocks(12, 12, 64, 768)                  # transposed Conv1D [hidden, 3 hidden]
+    with pytest.raises(qk.QkvnrError):
+        qk.qkvnr_fused_head_blocks(0, 0, 64, 0)
+    out = ctypes.c_int64(5)
+    assert qk.lib().qkvnr_fused_head_blocks(8, 2, 16, 100, ctypes.byref(out)) == qk.EINVAL and out.value == 0
+    assert qk.lib().qkvnr_fused_head_blocks(8, 2, 16, 192, None) == qk.EINVAL
+
+
+def test_ns_poly_argument_checks():
+    f = qk.lib().qkvnr_ns_poly
+    # dtype, blocks, d, gram, parts, first, scale, eps, p
+    ok = [qk.BF16, 48, 128, A, 11, 1, 1.0, 1e-7, B]
+
+    def call(**change):
+        a = list(ok)
+        for i, v in change.items():
+            a[int(i[1:])] = v
+        return f(*a, None)
+
+    assert call(i0=9) == qk.EINVAL
+    assert call(i1=-1) == qk.EINVAL
+    assert call(i2=129) == qk.EUNSUPPORTED
+    assert call(i2=0) == qk.EUNSUPPORTED
+    assert call(i4=0) == qk.EINVAL               # parts
+    assert call(i6=0.0) == qk.EINVAL             # scale
+    assert call(i7=-1.0) == qk.EINVAL            # eps
+    assert call(i3=A + 2) == qk.EALIGN
+    assert call(i3=A + 4) == qk.EALIGN
+    assert call(i8=0) == qk.EINVAL
+    assert call(i8=B + 1) == qk.EALIGN
+    assert call(i8=A + 64) == qk.EINVAL          # p overlaps gram
+    assert call(i1=0, i3=0, i8=0) == qk.OK         # no blocks: nothing is touched
+
+
+def test_gram_partials_argument_checks():
+    f = qk.lib().qkvnr_gram_partials
+    # blocks, d, cols, x, parts, out
+    ok = [48, 128, 4096, A, 11, B]
+
+    def call(**change):
+        a = list(ok)
+        for i, v in change.items():
+            a[int(i[1:])] = v
+        return f(*a, None)
+
+    assert call(i0=-1) == qk.EINVAL
+    assert call(i1=48) == qk.EUNSUPPORTED
+    assert call(i2=4100) == qk.EALIGN            # cols not a multiple of 8
+    assert call(i2=0) == qk.EALIGN
+    assert call(i4=0) == qk.EINVAL
+    assert call(i3=A + 8) == qk.EALIGN
+    assert call(i5=B + 2) == qk.EALIGN
+    assert call(i5=A + 4096) == qk.EINVAL         # out overlaps x
+    assert call(i0=0, i3=0, i5=0) == qk.OK
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     import qkv_split_head_amd._binding as b
     monkeypatch.setattr(b, "_lib", None)
