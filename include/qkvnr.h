@@ -257,7 +257,8 @@ int qkvnr_fused_head_blocks(int32_t n_q, int32_t n_kv, int32_t head_dim, int64_t
  *   cols    block width, a positive multiple of 8 (QKVNR_EALIGN otherwise).
  *   x       [blocks, d, cols] bf16, row-major, 16-byte aligned.
  *   parts   column slices, 1..65535: slice p covers columns
- *           [p * S, min(cols, (p + 1) * S)), S = ceil(ceil(cols / parts) / 16) * 16.
+ *           [p * S, min(cols, (p + 1) * S)), S = ceil(ceil(cols / parts) / 16) * 16;
+ *           S must be at most 512 (QKVNR_EINVAL otherwise).
  *   out     [blocks, parts, d, d] fp32, 4-byte aligned, must not overlap x;
  *           out[b][p] is block b's Gram matrix over slice p (zero for an empty slice).
  */

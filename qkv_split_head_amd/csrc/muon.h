@@ -30,42 +30,63 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // Partial Gram matrices of bf16 blocks: X [blocks, d, cols] (row stride cols),
 // out [blocks, parts, d, d] fp32, out[b][p] = X_b[:, S_p] X_b[:, S_p]^T over the
-// column slice S_p = [p * slice, min(cols, (p + 1) * slice)).  One workgroup per
-// (block, slice), d / 32 waves; wave w owns rows [32 w, 32 w + 32) and computes
-// their d / 32 tiles of 32 x 32 with v_mfma_f32_32x32x16_bf16.  Lane l's operand
-// is 8 consecutive columns of row (l mod 32) of a 32-row group, at column
-// offset 8 (l / 32) of each 16-column step; columns past `cols` read as zero.
+// column slice S_p = [p * slice, min(cols, (p + 1) * slice)), slice <= 512.
+// One workgroup per (block, slice), d / 32 waves.  The workgroup first copies
+// its d x slice piece into LDS with coalesced 16-byte loads (all issued before
+// any is used), rows padded to 64 chunks of 16 bytes and the chunks of row r
+// permuted by c ^ (r mod 16), so that the MFMA operand reads below (16 rows at
+// one chunk per pass) fall in 16 different bank groups.  Then wave w forms the
+// 32 x 32 tiles of its rows [32 w, 32 w + 32) with v_mfma_f32_32x32x16_bf16:
+// lane l's operand is the 8 columns at 8 (l / 32) of each 16-column step of
+// row l mod 32 of a 32-row group.  Columns past the slice read as zero.
+constexpr int kGramChunks = 64;  // 16-byte chunks per LDS row: 512 columns
 template <int D>
 __global__ __launch_bounds__(kWave * (D / 32)) void gram_partials_kernel(const uint16_t* __restrict__ x,
                                                                         int64_t cols, int64_t slice,
                                                                         float* __restrict__ out) {
-  constexpr int TILES = D / 32;
+  constexpr int TILES = D / 32, THREADS = kWave * TILES;
+  constexpr int PER = D * kGramChunks / THREADS;  // chunks each thread copies (32)
+  __shared__ uint4 lds[D * kGramChunks];
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x / kWave;
   const int64_t blk = blockIdx.x;
   const int part = blockIdx.y, parts = gridDim.y;
-  const int64_t k0 = part * slice, k1 = min(cols, k0 + slice);
-  const uint16_t* xb = x + blk * D * cols;
-  const int r = lane % 32, kh = (lane / 32) * 8;
+  const int64_t k0 = part * slice;
+  const int n8 = static_cast<int>(max<int64_t>(0, min<int64_t>(cols - k0, slice)) / 8);  // chunks of the slice
+  const uint16_t* xb = x + blk * D * cols + k0;
+  // copy in two halves of PER / 2 loads each (all of a half's loads go out first)
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint4 v[PER / 2];
+#pragma unroll
+    for (int j = 0; j < PER / 2; ++j) {
+      const int i = threadIdx.x + (h * (PER / 2) + j) * THREADS;
+      const int r = i / kGramChunks, c = i % kGramChunks;
+      v[j] = c < n8 ? ld16(xb + r * cols + c * 8) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int j = 0; j < PER / 2; ++j) {
+      const int i = threadIdx.x + (h * (PER / 2) + j) * THREADS;
+      const int r = i / kGramChunks, c = i % kGramChunks;
+      lds[r * kGramChunks + (c ^ (r & 15))] = v[j];
+    }
+  }
+  __syncthreads();
+  const int rr = lane % 32, ch = lane / 32;
   f32x16_t acc[TILES];
 #pragma unroll
   for (int t = 0; t < TILES; ++t) acc[t] = f32x16_t{};
-#pragma unroll 4
-  for (int64_t k = k0; k < k1; k += 16) {
-    const int64_t kk = k + kh;
-    const bool in = kk < k1;  // cols is a multiple of 8: a lane's 8 columns are all in or all out
-    uint4 av = make_uint4(0u, 0u, 0u, 0u);
-    if (in) av = ld16(xb + (32 * w + r) * cols + kk);
-    uint4 bv[TILES];
+  const int steps = (n8 + 1) / 2;  // 16-column steps holding data
+  for (int s = 0; s < steps; ++s) {
+    const int c = 2 * s + ch;
+    const int ra = 32 * w + rr;
+    const bf16x8_t a = __builtin_bit_cast(bf16x8_t, lds[ra * kGramChunks + (c ^ (ra & 15))]);
 #pragma unroll
     for (int t = 0; t < TILES; ++t) {
-      bv[t] = make_uint4(0u, 0u, 0u, 0u);
-      if (in) bv[t] = ld16(xb + (32 * t + r) * cols + kk);
+      const int rb = 32 * t + rr;
+      const bf16x8_t b = __builtin_bit_cast(bf16x8_t, lds[rb * kGramChunks + (c ^ (rb & 15))]);
+      acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[t], 0, 0, 0);
     }
-    const bf16x8_t a = __builtin_bit_cast(bf16x8_t, av);
-#pragma unroll
-    for (int t = 0; t < TILES; ++t)
-      acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bv[t]), acc[t], 0, 0, 0);
   }
   // C register e of lane l is row 8 (e / 4) + 4 (l / 32) + e % 4, column l % 32 of the tile
   float* o = out + (blk * parts + part) * D * D;

@@ -518,6 +518,11 @@ int qkvnr_gram_partials(int64_t blocks, int32_t d, int64_t cols, const void* x, 
     return fail(QKVNR_EUNSUPPORTED, "block side %d: kernels exist for 32, 64, 96 and 128", d);
   if (cols < 1 || cols % 8) return fail(QKVNR_EALIGN, "cols %lld must be a positive multiple of 8", (long long)cols);
   if (parts < 1 || parts > 65535) return fail(QKVNR_EINVAL, "parts %d out of [1, 65535]", parts);
+  // column slices of a multiple of 16, as even as that allows, at most 512 columns (one LDS piece)
+  const int64_t slice = ((cols + parts - 1) / parts + 15) / 16 * 16;
+  if (slice > 8 * kGramChunks)
+    return fail(QKVNR_EINVAL, "%d parts give slices of %lld columns: at most %d fit (use parts >= %lld)", parts,
+                (long long)slice, 8 * kGramChunks, (long long)((cols + 8 * kGramChunks - 1) / (8 * kGramChunks)));
   if (blocks == 0) return QKVNR_OK;
   if (int rc = need16(x, "x")) return rc;
   if (int rc = need4(out, "out")) return rc;
@@ -525,8 +530,6 @@ int qkvnr_gram_partials(int64_t blocks, int32_t d, int64_t cols, const void* x, 
   if (overlaps({x, blocks * d * cols * 2}, {out, n_out * 4})) return fail(QKVNR_EINVAL, "out overlaps x");
   int cus = 0;
   if (int rc = current_device(&cus)) return rc;
-  // column slices of a multiple of 16, as even as that allows
-  const int64_t slice = ((cols + parts - 1) / parts + 15) / 16 * 16;
   const dim3 g(static_cast<uint32_t>(blocks), static_cast<uint32_t>(parts));
   const auto* xs = static_cast<const uint16_t*>(x);
   switch (d) {
