@@ -251,14 +251,14 @@ int qkvnr_fused_head_blocks(int32_t n_q, int32_t n_kv, int32_t head_dim, int64_t
  * the first product of each Newton-Schulz step (and G G^T for the first).
  * Both factors are rows of X, read along the long side; v_mfma_f32_32x32x16_bf16.
  *
- *   blocks  number of blocks, >= 0 (0 is a no-op).
+ *   blocks  number of blocks, 0 .. 2^31 - 1 (0 is a no-op).
  *   d       block side (rows of each block): 32, 64, 96 or 128 (others
  *           QKVNR_EUNSUPPORTED).
- *   cols    block width, a positive multiple of 8 (QKVNR_EALIGN otherwise).
+ *   cols    block width, a positive multiple of 8 (QKVNR_EALIGN otherwise), at
+ *           most 2^30 (QKVNR_EINVAL otherwise).
  *   x       [blocks, d, cols] bf16, row-major, 16-byte aligned.
  *   parts   column slices, 1..65535: slice p covers columns
- *           [p * S, min(cols, (p + 1) * S)), S = ceil(ceil(cols / parts) / 16) * 16;
- *           S must be at most 512 (QKVNR_EINVAL otherwise).
+ *           [p * S, min(cols, (p + 1) * S)), S = ceil(ceil(cols / parts) / 16) * 16.
  *   out     [blocks, parts, d, d] fp32, 4-byte aligned, must not overlap x;
  *           out[b][p] is block b's Gram matrix over slice p (zero for an empty slice).
  */
@@ -279,9 +279,8 @@ int qkvnr_gram_partials(int64_t blocks, int32_t d, int64_t cols, const void* x, 
  *   dtype   QKVNR_BF16 or QKVNR_FP32: the type of p.
  *   blocks  number of blocks, >= 0 (0 is a no-op).
  *   d       block side, 1..128 (others QKVNR_EUNSUPPORTED).
- *   gram    [blocks, parts, d, d] fp32, row-major, 16-byte aligned.  With
- *           parts > 1 it is also written: each block's partial 0 becomes the
- *           sum of its partials (the others are left as they were).
+ *   gram    [blocks, parts, d, d] fp32, row-major, 16-byte aligned; read
+ *           only (the partials are added in order as they are loaded).
  *   parts   >= 1.
  *   p       out [blocks, d, d] in dtype, row-major; must not overlap gram.
  */

@@ -11,7 +11,7 @@
 // (d = the block's short side).  gram_partials_kernel forms A with MFMA from
 // X's rows (both operands of X X^T are rows of X, read 16 bytes at a time along
 // the long side), as partial sums over column slices; ns_poly_kernel adds the
-// partials (gram_reduce_kernel) and forms P, folding in the first step's
+// partials as it loads them and forms P, folding in the first step's
 // normalisation (||G||_F^2 is the trace of G G^T: A is divided by its square
 // and P by the norm) and the last step's scale; the update P X is a plain
 // batched GEMM.
@@ -30,114 +30,176 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // Partial Gram matrices of bf16 blocks: X [blocks, d, cols] (row stride cols),
 // out [blocks, parts, d, d] fp32, out[b][p] = X_b[:, S_p] X_b[:, S_p]^T over the
-// column slice S_p = [p * slice, min(cols, (p + 1) * slice)), slice <= 512.
-// One workgroup per (block, slice), d / 32 waves.  The workgroup first copies
-// its d x slice piece into LDS with coalesced 16-byte loads (all issued before
-// any is used), rows padded to 64 chunks of 16 bytes and the chunks of row r
-// permuted by c ^ (r mod 16), so that the MFMA operand reads below (16 rows at
-// one chunk per pass) fall in 16 different bank groups.  Then wave w forms the
-// 32 x 32 tiles of its rows [32 w, 32 w + 32) with v_mfma_f32_32x32x16_bf16:
-// lane l's operand is the 8 columns at 8 (l / 32) of each 16-column step of
-// row l mod 32 of a 32-row group.  Columns past the slice read as zero.
-constexpr int kGramChunks = 64;  // 16-byte chunks per LDS row: 512 columns
+// column slice S_p = [p * slice, min(cols, (p + 1) * slice)).
+// One workgroup per (block, slice), d / 32 waves, streams the block's d rows
+// through LDS in chunks of 64 columns.  Each thread loads 4 pieces of 16 bytes
+// of a chunk (8 adjacent threads cover the 128 bytes of one row), kGramDepth
+// chunks ahead, into registers, and writes a chunk to one of two LDS buffers
+// just before it is used; then wave w adds the chunk's products to the tiles
+// (w, t), t < d / 32, of 32 x 32 with v_mfma_f32_32x32x16_bf16: in step s (16
+// columns) lane l's operand is piece 2 s + l / 32 of row l mod 32 of a 32-row
+// group.  Piece q of row r sits at position q ^ ((r / 2) mod 8) of the row in
+// LDS, so the 16 rows that one operand read serves at a time hit every bank
+// once.  Columns past the slice are zero.  The barrier between chunks orders
+// LDS only: the loads of later chunks stay in flight across it.
+constexpr int kGramChunk = 64;  // columns per LDS chunk: 8 pieces of 16 bytes a row
+#ifndef QKVNR_GRAM_DEPTH
+#define QKVNR_GRAM_DEPTH 2
+#endif
+constexpr int kGramDepth = QKVNR_GRAM_DEPTH;  // chunks in flight per thread
+static_assert(kGramDepth >= 2 && kGramDepth % 2 == 0 && kGramDepth <= 8, "even Gram prefetch depth 2..8");
+
 template <int D>
-__global__ __launch_bounds__(kWave * (D / 32)) void gram_partials_kernel(const uint16_t* __restrict__ x,
-                                                                        int64_t cols, int64_t slice,
-                                                                        float* __restrict__ out) {
-  constexpr int TILES = D / 32, THREADS = kWave * TILES;
-  constexpr int PER = D * kGramChunks / THREADS;  // chunks each thread copies (32)
-  __shared__ uint4 lds[D * kGramChunks];
+__global__ __launch_bounds__(kWave * (D / 32)) void gram_partials_kernel(const uint16_t* __restrict__ x, int cols,
+                                                                        int slice, float* __restrict__ out) {
+  constexpr int T = D / 32, THREADS = kWave * T, PIECES = kGramChunk / 8;
+  constexpr int PER = D * PIECES / THREADS;  // pieces each thread loads per chunk (4)
+  __shared__ uint4 lds[2][D * PIECES];
   const int lane = threadIdx.x & (kWave - 1);
-  const int w = threadIdx.x / kWave;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int64_t blk = blockIdx.x;
   const int part = blockIdx.y, parts = gridDim.y;
-  const int64_t k0 = part * slice;
-  const int n8 = static_cast<int>(max<int64_t>(0, min<int64_t>(cols - k0, slice)) / 8);  // chunks of the slice
-  const uint16_t* xb = x + blk * D * cols + k0;
-  // copy in two halves of PER / 2 loads each (all of a half's loads go out first)
+  const int k0 = part * slice, kend = min(cols, k0 + slice);
+  const int chunks = kend > k0 ? (kend - k0 + kGramChunk - 1) / kGramChunk : 0;
+  const int q = threadIdx.x % PIECES;
+  const uint16_t* rp[PER];
+  int slot[PER];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    uint4 v[PER / 2];
-#pragma unroll
-    for (int j = 0; j < PER / 2; ++j) {
-      const int i = threadIdx.x + (h * (PER / 2) + j) * THREADS;
-      const int r = i / kGramChunks, c = i % kGramChunks;
-      v[j] = c < n8 ? ld16(xb + r * cols + c * 8) : make_uint4(0u, 0u, 0u, 0u);
-    }
-#pragma unroll
-    for (int j = 0; j < PER / 2; ++j) {
-      const int i = threadIdx.x + (h * (PER / 2) + j) * THREADS;
-      const int r = i / kGramChunks, c = i % kGramChunks;
-      lds[r * kGramChunks + (c ^ (r & 15))] = v[j];
-    }
+  for (int j = 0; j < PER; ++j) {
+    const int r = (threadIdx.x + j * THREADS) / PIECES;
+    rp[j] = x + (blk * D + r) * cols;
+    slot[j] = r * PIECES + (q ^ ((r >> 1) & 7));
   }
-  __syncthreads();
-  const int rr = lane % 32, ch = lane / 32;
-  f32x16_t acc[TILES];
+  auto load = [&](int c, uint4 (&v)[PER]) {
+    const int col = min(k0 + c * kGramChunk + 8 * q, cols - 8);  // clamped into the row
 #pragma unroll
-  for (int t = 0; t < TILES; ++t) acc[t] = f32x16_t{};
-  const int steps = (n8 + 1) / 2;  // 16-column steps holding data
-  for (int s = 0; s < steps; ++s) {
-    const int c = 2 * s + ch;
-    const int ra = 32 * w + rr;
-    const bf16x8_t a = __builtin_bit_cast(bf16x8_t, lds[ra * kGramChunks + (c ^ (ra & 15))]);
+    for (int j = 0; j < PER; ++j) v[j] = ld16(rp[j] + col);
+  };
+  auto store = [&](int c, const uint4 (&v)[PER], uint4* buf) {
+    // zero past the slice with a mask, not a branch (a branch here makes the compiler wait for every load)
+    const uint32_t m = k0 + c * kGramChunk + 8 * q < kend ? 0xffffffffu : 0u;
 #pragma unroll
-    for (int t = 0; t < TILES; ++t) {
-      const int rb = 32 * t + rr;
-      const bf16x8_t b = __builtin_bit_cast(bf16x8_t, lds[rb * kGramChunks + (c ^ (rb & 15))]);
-      acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[t], 0, 0, 0);
+    for (int j = 0; j < PER; ++j) buf[slot[j]] = make_uint4(v[j].x & m, v[j].y & m, v[j].z & m, v[j].w & m);
+  };
+  const int rr = lane % 32, h = lane / 32, sw = (rr >> 1) & 7;  // rows 32 t + rr share the swizzle
+  f32x16_t acc[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) acc[t] = f32x16_t{};
+  constexpr int STEPS = kGramChunk / 16;
+  uint4 a[STEPS], b[STEPS][T];
+  auto reads = [&](const uint4* buf) {  // every operand of the chunk: one LDS round trip, not one a step
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+      const int pos = (2 * st + h) ^ sw;
+      a[st] = buf[(32 * w + rr) * PIECES + pos];
+#pragma unroll
+      for (int t = 0; t < T; ++t) b[st][t] = buf[(32 * t + rr) * PIECES + pos];
+    }
+  };
+  auto mfmas = [&](int st) {
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+      acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[st]),
+                                                       __builtin_bit_cast(bf16x8_t, b[st][t]), acc[t], 0, 0, 0);
+  };
+  auto lds_barrier = [] {  // orders LDS only: later chunks' loads stay in flight across it
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  };
+  // chunk c is loaded into v[c mod depth] (in chunk order, so that each store waits for its own
+  // chunk only), stored to LDS buffer c mod 2 one chunk ahead of its products, and the store and
+  // the next loads are issued between the products of the chunk before, while the matrix unit works
+  uint4 v[kGramDepth][PER];
+#pragma unroll
+  for (int j = 0; j < kGramDepth; ++j) {
+    load(j, v[j]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  store(0, v[0], lds[0]);
+  load(kGramDepth, v[0]);
+  lds_barrier();
+  for (int c0 = 0; c0 < chunks; c0 += kGramDepth) {
+#pragma unroll
+    for (int j = 0; j < kGramDepth; ++j) {
+      // loads, stores and barriers on every path (chunks past the slice are zeros); products for
+      // chunks of the slice only (the same for the whole workgroup)
+      const int c = c0 + j;
+      const bool live = c < chunks;
+      if (live) {
+        reads(lds[j & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      store(c + 1, v[(j + 1) % kGramDepth], lds[(j + 1) & 1]);
+      load(c + 1 + kGramDepth, v[(j + 1) % kGramDepth]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (live) {
+#pragma unroll
+        for (int st = 1; st < STEPS; ++st) mfmas(st);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      lds_barrier();
     }
   }
   // C register e of lane l is row 8 (e / 4) + 4 (l / 32) + e % 4, column l % 32 of the tile
   float* o = out + (blk * parts + part) * D * D;
 #pragma unroll
-  for (int t = 0; t < TILES; ++t)
+  for (int t = 0; t < T; ++t)
 #pragma unroll
     for (int e = 0; e < 16; ++e)
-      o[(32 * w + 8 * (e / 4) + 4 * (lane / 32) + e % 4) * D + 32 * t + lane % 32] = acc[t][e];
+      o[(32 * w + 8 * (e / 4) + 4 * h + e % 4) * D + 32 * t + rr] = acc[t][e];
 }
 
-// Sums each block's Gram partials into its partial 0 (in place): one thread
-// per element of A, all blocks at once (n = d * d).
-__global__ __launch_bounds__(kNsThreads) void gram_reduce_kernel(float* __restrict__ gram, int parts, int n,
-                                                                 int64_t total) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * kNsThreads + threadIdx.x;
-  if (i >= total) return;
-  float* g = gram + (i / n) * parts * n + i % n;
-  float s = g[0];
-  for (int p = 1; p < parts; ++p) s += g[static_cast<int64_t>(p) * n];
-  g[0] = s;
-}
-
-// P from the Gram matrix A of each block (held in the block's partial 0, i.e.
-// at gram + b * parts * d * d): one workgroup per (block, group of 32 rows of
-// P).  The workgroup copies A into LDS and forms its rows of A^2 in 4 x 4
-// patches (A is symmetric, so both factors are read along rows of A).
+// P from the Gram matrix A of each block (the sum of its partials, at
+// gram + b * parts * d * d): one workgroup per (block, group of 32 rows of P).
+// The workgroup adds the partials into LDS and forms its rows of A^2 in 4 x 4
+// patches (A is symmetric, so both factors are read along rows of A, 16 bytes
+// at a time).
 // DT > 0 fixes d at compile time (the common side 128); 0 takes it from `d_rt`.
 template <typename OUT, int DT>
 __global__ __launch_bounds__(kNsThreads) void ns_poly_kernel(const float* __restrict__ gram, OUT* __restrict__ out,
                                                             int d_rt, int parts, int first, float last_scale,
                                                             float eps) {
   const int d = DT > 0 ? DT : d_rt;
-  constexpr int LD = kNsMaxD + 1;  // odd row stride: the column patches of a wave read different banks
-  __shared__ float A[kNsMaxD * LD];
+  constexpr int LD = kNsMaxD + 4;  // rows 16-byte aligned for float4 reads
+  __shared__ __align__(16) float A[kNsMaxD * LD];
   __shared__ float red[kNsThreads / kWave];
   const int64_t blk = blockIdx.x;
   const int row0 = blockIdx.y * 32, rows = min(32, d - row0);
   const float* g = gram + blk * parts * d * d;
-  {  // all of the thread's loads first, then the LDS writes (one round trip, not one per element)
-    constexpr int CH = kNsMaxD * kNsMaxD / kNsThreads;
-    const int n = d * d;
-    float v[CH];
+  if (d % 4 == 0) {  // 16-byte loads (a row holds whole groups of 4); each part's loads go out before they are added
+    constexpr int CH = kNsMaxD * kNsMaxD / 4 / kNsThreads;
+    const int n4 = d * d / 4;
+    const float4* g4 = reinterpret_cast<const float4*>(g);
+    float4 v[CH];
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
       const int i = threadIdx.x + j * kNsThreads;
-      v[j] = i < n ? g[i] : 0.0f;
+      v[j] = i < n4 ? g4[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+    for (int pt = 1; pt < parts; ++pt) {  // partials added in order
+      float4 u[CH];
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        const int i = threadIdx.x + j * kNsThreads;
+        u[j] = i < n4 ? g4[static_cast<int64_t>(pt) * n4 + i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      }
+#pragma unroll
+      for (int j = 0; j < CH; ++j) v[j] = make_float4(v[j].x + u[j].x, v[j].y + u[j].y, v[j].z + u[j].z, v[j].w + u[j].w);
     }
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-      const int i = threadIdx.x + j * kNsThreads;
-      if (i < n) A[(i / d) * LD + i % d] = v[j];
+      const int i = 4 * (threadIdx.x + j * kNsThreads);
+      if (i < d * d) *reinterpret_cast<float4*>(&A[(i / d) * LD + i % d]) = v[j];
+    }
+  } else {  // one value at a time
+    const int n = d * d;
+    for (int i = threadIdx.x; i < n; i += kNsThreads) {
+      float a = g[i];
+      for (int pt = 1; pt < parts; ++pt) a += g[static_cast<int64_t>(pt) * n + i];
+      A[(i / d) * LD + i % d] = a;
     }
   }
   __syncthreads();
@@ -163,13 +225,13 @@ __global__ __launch_bounds__(kNsThreads) void ns_poly_kernel(const float* __rest
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+    // A is symmetric, so both factors of (A^2)[r][c] = sum_k A[r][k] A[k][c] are read along row k,
+    // 4 adjacent values at a time (past column d they are never stored into P)
+#pragma unroll 4
     for (int k = 0; k < d; ++k) {
-      float ar[4], ac[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ar[i] = r0 + i < d ? A[(r0 + i) * LD + k] : 0.0f;
-        ac[i] = c0 + i < d ? A[(c0 + i) * LD + k] : 0.0f;  // A[k][c] = A[c][k]
-      }
+      const float4 r4 = *reinterpret_cast<const float4*>(&A[k * LD + r0]);
+      const float4 c4 = *reinterpret_cast<const float4*>(&A[k * LD + c0]);
+      const float ar[4] = {r4.x, r4.y, r4.z, r4.w}, ac[4] = {c4.x, c4.y, c4.z, c4.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll

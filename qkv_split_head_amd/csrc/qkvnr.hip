@@ -517,12 +517,8 @@ int qkvnr_gram_partials(int64_t blocks, int32_t d, int64_t cols, const void* x, 
   if (d != 32 && d != 64 && d != 96 && d != 128)
     return fail(QKVNR_EUNSUPPORTED, "block side %d: kernels exist for 32, 64, 96 and 128", d);
   if (cols < 1 || cols % 8) return fail(QKVNR_EALIGN, "cols %lld must be a positive multiple of 8", (long long)cols);
+  if (cols > (1 << 30)) return fail(QKVNR_EINVAL, "cols %lld above 2^30", (long long)cols);
   if (parts < 1 || parts > 65535) return fail(QKVNR_EINVAL, "parts %d out of [1, 65535]", parts);
-  // column slices of a multiple of 16, as even as that allows, at most 512 columns (one LDS piece)
-  const int64_t slice = ((cols + parts - 1) / parts + 15) / 16 * 16;
-  if (slice > 8 * kGramChunks)
-    return fail(QKVNR_EINVAL, "%d parts give slices of %lld columns: at most %d fit (use parts >= %lld)", parts,
-                (long long)slice, 8 * kGramChunks, (long long)((cols + 8 * kGramChunks - 1) / (8 * kGramChunks)));
   if (blocks == 0) return QKVNR_OK;
   if (int rc = need16(x, "x")) return rc;
   if (int rc = need4(out, "out")) return rc;
@@ -530,13 +526,16 @@ int qkvnr_gram_partials(int64_t blocks, int32_t d, int64_t cols, const void* x, 
   if (overlaps({x, blocks * d * cols * 2}, {out, n_out * 4})) return fail(QKVNR_EINVAL, "out overlaps x");
   int cus = 0;
   if (int rc = current_device(&cus)) return rc;
+  // column slices of a multiple of 16, as even as that allows
+  const int sl = static_cast<int>(((cols + parts - 1) / parts + 15) / 16 * 16);
   const dim3 g(static_cast<uint32_t>(blocks), static_cast<uint32_t>(parts));
   const auto* xs = static_cast<const uint16_t*>(x);
+  const int c = static_cast<int>(cols);
   switch (d) {
-    case 32: hipLaunchKernelGGL(gram_partials_kernel<32>, g, dim3(kWave * 1), 0, stream, xs, cols, slice, out); break;
-    case 64: hipLaunchKernelGGL(gram_partials_kernel<64>, g, dim3(kWave * 2), 0, stream, xs, cols, slice, out); break;
-    case 96: hipLaunchKernelGGL(gram_partials_kernel<96>, g, dim3(kWave * 3), 0, stream, xs, cols, slice, out); break;
-    default: hipLaunchKernelGGL(gram_partials_kernel<128>, g, dim3(kWave * 4), 0, stream, xs, cols, slice, out); break;
+    case 32: hipLaunchKernelGGL(gram_partials_kernel<32>, g, dim3(kWave * 1), 0, stream, xs, c, sl, out); break;
+    case 64: hipLaunchKernelGGL(gram_partials_kernel<64>, g, dim3(kWave * 2), 0, stream, xs, c, sl, out); break;
+    case 96: hipLaunchKernelGGL(gram_partials_kernel<96>, g, dim3(kWave * 3), 0, stream, xs, c, sl, out); break;
+    default: hipLaunchKernelGGL(gram_partials_kernel<128>, g, dim3(kWave * 4), 0, stream, xs, c, sl, out); break;
   }
   return launched("Gram partials");
 }
@@ -557,12 +556,6 @@ int qkvnr_ns_poly(int32_t dtype, int64_t blocks, int32_t d, float* gram, int32_t
   if (overlaps({gram, n * parts * 4}, {p, n * elem_bytes(dtype)})) return fail(QKVNR_EINVAL, "p overlaps gram");
   int cus = 0;
   if (int rc = current_device(&cus)) return rc;
-  if (parts > 1) {  // the partials are summed into each block's partial 0
-    const int64_t total = blocks * d * d;
-    hipLaunchKernelGGL(gram_reduce_kernel, dim3(static_cast<uint32_t>((total + kNsThreads - 1) / kNsThreads)),
-                       dim3(kNsThreads), 0, stream, const_cast<float*>(gram), parts, d * d, total);
-    if (int rc = launched("Gram reduction")) return rc;
-  }
   const dim3 grid(static_cast<uint32_t>(blocks), static_cast<uint32_t>((d + 31) / 32));
   const int fi = first ? 1 : 0;
   if (dtype == QKVNR_BF16) {

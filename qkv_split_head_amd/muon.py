@@ -37,9 +37,9 @@ def fused_head_blocks(n_q: int, n_kv: int, head_dim: int, weight_rows: int) -> i
 
 
 def _gram_parts(nb: int, cols: int) -> int:
-    """Column slices for the Gram kernel: slices of at most 512 columns (one LDS piece), and
-    more of them when there are few blocks, down to slices of 128 columns."""
-    return max(-(-cols // 512), min(-(-cols // 128), -(-512 // nb)))
+    """Column slices for the Gram kernel (one workgroup per block and slice): about one
+    workgroup per CU, slices of >= 512 columns."""
+    return max(1, min(256 // nb, cols // 512))
 
 
 def _newton_schulz_blocks(X: torch.Tensor, scale: float, steps: int, eps: float) -> torch.Tensor:

@@ -73,8 +73,11 @@ def test_sectioned_and_interleaved_give_the_same_blocks_bitwise(dtype):
                        us[order].view(torch.int16) if dtype == torch.bfloat16 else us[order])
 
 
+# the 4 waves of a tile take runs of 64 columns in turn; 1320 and 1064 columns end a wave's runs
+# with an odd and an even count of whole runs before a partial one
 @pytest.mark.parametrize("blocks,d,cols,parts", [(3, 32, 200, 3), (2, 64, 4096, 11), (5, 96, 72, 1),
-                                                  (48, 128, 4096, 11), (1, 128, 24, 4)])
+                                                  (48, 128, 4096, 11), (1, 128, 24, 4), (48, 128, 4096, 1),
+                                                  (2, 128, 1320, 1), (3, 64, 1064, 1), (7, 96, 3000, 2)])
 def test_gram_partials_match_the_products(blocks, d, cols, parts):
     # each slice's Gram matrix, and their sum, against fp64 products of the same bf16 values
     rng = np.random.default_rng(blocks * d + cols)
