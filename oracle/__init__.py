@@ -21,3 +21,4 @@ from .reference import (  # noqa: F401
     staged_then_scatter,
 )
 from .mla_drafter import absorb, drafter_layer  # noqa: F401,E402
+from .projection import project, projected_forward_gqa  # noqa: F401,E402

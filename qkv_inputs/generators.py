@@ -342,3 +342,73 @@ def mla_drafter_layer(
         w_uk=w_uk, w_kv_a=w_kva, w_kv_a_ln=w_kva_ln, positions=pos, block_table=table, tokens_per_req=T_req,
         page_size=page_size, num_pages=num_pages, extra={"ctx": ctx},
     )
+
+
+@dataclass
+class ProjectionInputs:
+    """The QKV projection's input and weight, plus the region's own parameters.
+
+    ``x`` is ``[T, hidden]``; ``w_qkv`` is ``[(n_q + 2 n_kv) * head_dim, hidden]``
+    (``[out, in]``: the packed output is ``x @ w_qkv^T``), its head blocks of
+    ``head_dim`` rows in the layout's order (``kind``).  bf16 arrays are ``uint16``
+    bit patterns.  The weight is N(0, 1/hidden), so the packed values are O(1);
+    norm weights are N(1, 0.1).
+    """
+
+    name: str
+    kind: str
+    T: int
+    hidden: int
+    n_kv: int
+    q_per_kv: int
+    head_dim: int
+    rope: bool
+    eps: float
+    theta: float
+    x: np.ndarray
+    w_qkv: np.ndarray
+    q_norm_w: np.ndarray
+    k_norm_w: np.ndarray
+    positions: np.ndarray
+
+    @property
+    def n_q(self) -> int:
+        return self.n_kv * self.q_per_kv
+
+    @property
+    def width(self) -> int:
+        return (self.n_q + 2 * self.n_kv) * self.head_dim
+
+
+def projection(
+    kind: str,
+    T: int,
+    hidden: int,
+    n_kv: int,
+    q_per_kv: int,
+    head_dim: int,
+    *,
+    rope: bool = True,
+    theta: float = 1e6,
+    eps: float = 1e-6,
+    seed: int = 60,
+    positions: str = "arange",
+    max_pos: int = 131072,
+    name: str = "projection",
+) -> ProjectionInputs:
+    """bf16 projection inputs.  Draw order: x, w_qkv, q norm weight, k norm weight, positions."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    width = (n_kv * q_per_kv + 2 * n_kv) * head_dim
+    x = _draw(rng, (T, hidden), "bf16")
+    w = _draw(rng, (width, hidden), "bf16", 0.0, float(hidden) ** -0.5)
+    wq = _draw(rng, (head_dim,), "bf16", 1.0, 0.1)
+    wk = _draw(rng, (head_dim,), "bf16", 1.0, 0.1)
+    if positions == "arange":
+        pos = np.arange(T, dtype=np.int32)
+    elif positions == "random":
+        pos = rng.integers(0, max_pos, size=T, dtype=np.int64).astype(np.int32)
+    else:
+        raise ValueError(positions)
+    return ProjectionInputs(name=name, kind=kind, T=T, hidden=hidden, n_kv=n_kv, q_per_kv=q_per_kv,
+                            head_dim=head_dim, rope=rope, eps=eps, theta=theta, x=x, w_qkv=w,
+                            q_norm_w=wq, k_norm_w=wk, positions=pos)

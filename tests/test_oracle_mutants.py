@@ -1,7 +1,7 @@
 """The oracle's pins catch plausible mistakes (CPU only).
 
 Each case plants one mistake in a temporary copy of ``oracle/reference.py``,
-``oracle/mla_drafter.py`` or ``oracle/muon.py``
+``oracle/mla_drafter.py``, ``oracle/muon.py`` or ``oracle/projection.py``
 (a dropped term, a wrong sign, a wrong index, a swapped operand) and runs the
 pin suite against that copy in a subprocess: the suite must fail.  Nothing
 here touches the GPU or the HIP library.
@@ -72,6 +72,19 @@ MUON_MUTANTS = {
 }
 MUON_SRC = os.path.join(ROOT, "oracle", "muon.py")
 
+# mistakes in the fused projection oracle, caught by its own pin file
+PROJ_MUTANTS = {
+    "projection_not_transposed": ("return to_f64(x, dtype) @ to_f64(w_qkv, dtype).T",
+                                  "return to_f64(x, dtype) @ to_f64(w_qkv, dtype)[:, :to_f64(x, dtype).shape[1]]"),
+    "projection_rows_reversed": ("return to_f64(x, dtype) @ to_f64(w_qkv, dtype).T",
+                                 "return to_f64(x, dtype) @ to_f64(w_qkv, dtype)[::-1].T"),
+    "v_from_k_heads": ("q[t0:t1], k[t0:t1], v[t0:t1] = qn, kn, v_raw", "q[t0:t1], k[t0:t1], v[t0:t1] = qn, kn, k_raw"),
+    "q_norm_uses_k_weight": ("qn = rmsnorm(q_raw, wq, eps)", "qn = rmsnorm(q_raw, wk, eps)"),
+    "split_always_sectioned": ("q_raw, k_raw, v_raw = split(Y, kind, n_kv, q_per_kv, D)",
+                               "q_raw, k_raw, v_raw = split(Y, \"sectioned\", n_kv, q_per_kv, D)"),
+}
+PROJ_SRC = os.path.join(ROOT, "oracle", "projection.py")
+
 
 def _run(name, old, new, tmp, src_path=SRC, pins="test_oracle_pins.py"):
     src = open(src_path).read()
@@ -92,6 +105,7 @@ def test_every_planted_mistake_fails_a_pin(tmp_path):
     jobs = [(n, o, w, SRC, "test_oracle_pins.py") for n, (o, w) in MUTANTS.items()]
     jobs += [(n, o, w, DRAFTER_SRC, "test_oracle_mla_drafter.py") for n, (o, w) in DRAFTER_MUTANTS.items()]
     jobs += [(n, o, w, MUON_SRC, "test_oracle_muon.py") for n, (o, w) in MUON_MUTANTS.items()]
+    jobs += [(n, o, w, PROJ_SRC, "test_oracle_projection.py") for n, (o, w) in PROJ_MUTANTS.items()]
     with ThreadPoolExecutor(max_workers=4) as ex:
         results = list(ex.map(lambda j: _run(j[0], j[1], j[2], str(tmp_path), j[3], j[4]), jobs))
     survivors = [(n, tail) for n, rc, tail in results if rc != 1]
