@@ -287,6 +287,34 @@ int qkvnr_gram_partials(int64_t blocks, int32_t d, int64_t cols, const void* x, 
 int qkvnr_ns_poly(int32_t dtype, int64_t blocks, int32_t d, float* gram, int32_t parts,
                   int32_t first, float scale, float eps, void* p, hipStream_t stream);
 
+/*
+ * The QKV projection with the forward region fused into its epilogue.
+ * (torchtitan page: Problem item 1, the region's input is the packed output of
+ *  the attention's QKV projection; Results, the region is timed with the GEMMs
+ *  left out.)
+ * packed = x w_qkv^T is formed in fp32 and never stored or rounded; each of its
+ * head blocks is split out as qkvnr_forward splits the packed input, q and k
+ * get qkvnr_forward's per-head RMSNorm and RoPE, v is rounded once, and q, k, v
+ * are written as qkvnr_forward writes them.
+ *
+ *   layout     kind QKVNR_INTERLEAVED or QKVNR_SECTIONED (others
+ *              QKVNR_EUNSUPPORTED), dtype QKVNR_BF16 (QKVNR_FP32 is
+ *              QKVNR_EUNSUPPORTED), T, n_kv, q_per_kv, head_dim, rope_dim and
+ *              width as for qkvnr_forward; in_row_stride is not used (there is
+ *              no packed tensor) but must pass the same check (>= width).
+ *   hidden     columns of x and w_qkv: a positive multiple of 64, at most 2^30
+ *              (QKVNR_EINVAL otherwise).
+ *   x          [T, hidden] bf16, row-major, 16-byte aligned.
+ *   w_qkv      [width, hidden] bf16, row-major, 16-byte aligned: row j is packed
+ *              column j, so its head blocks follow the layout's order.
+ *   positions, q_norm_w, k_norm_w, eps, theta, q, k, v: as for qkvnr_forward
+ *              (v is x w_v^T rounded once, not a copy).
+ * Outputs must not overlap any input (QKVNR_EINVAL).  T == 0 enqueues nothing.
+ */
+int qkvnr_proj_forward(const qkvnr_layout* layout, int64_t hidden, const void* x, const void* w_qkv,
+                       const int32_t* positions, const void* q_norm_w, const void* k_norm_w, float eps,
+                       double theta, void* q, void* k, void* v, hipStream_t stream);
+
 /* Static text for a return code.  For QKVNR_EHIP and the validation errors it
  * returns the last detailed message recorded on the calling thread. */
 const char* qkvnr_strerror(int code);

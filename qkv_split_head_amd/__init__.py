@@ -7,7 +7,8 @@ named like the C entry points (``qkvnr_forward``, ``qkvnr_backward``,
 ``forward_latent_paged`` also allocate the outputs; ``rope_inplace`` rotates a
 tensor's rope parts in place.  ``mla_drafter`` runs an MLA drafter layer's kv
 path beside its q path on two streams; ``muon`` runs per-head Newton-Schulz
-on fused QKV weights.
+on fused QKV weights; ``proj_forward`` (``qkvnr_proj_forward``) runs the
+QKV projection with the split, norms and RoPE in its epilogue.
 """
 from ._binding import (  # noqa: F401
     BF16,
@@ -32,6 +33,7 @@ from ._binding import (  # noqa: F401
     header_functions,
     latent_layout,
     lib,
+    proj_forward,
     qkvnr_backward,
     qkvnr_backward_workspace_bytes,
     qkvnr_forward,
@@ -39,6 +41,7 @@ from ._binding import (  # noqa: F401
     qkvnr_fused_head_blocks,
     qkvnr_gram_partials,
     qkvnr_ns_poly,
+    qkvnr_proj_forward,
     qkvnr_rope_inplace,
     rope_inplace,
     qkvnr_version,

@@ -88,6 +88,9 @@ def lib() -> ctypes.CDLL:
         L.qkvnr_ns_poly.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, vp, ctypes.c_int32,
                                     ctypes.c_int32, ctypes.c_float, ctypes.c_float, vp, vp]
         L.qkvnr_ns_poly.restype = ctypes.c_int
+        L.qkvnr_proj_forward.argtypes = [lp, ctypes.c_int64, vp, vp, i32p, vp, vp, ctypes.c_float, ctypes.c_double,
+                                         vp, vp, vp, vp]
+        L.qkvnr_proj_forward.restype = ctypes.c_int
         L.qkvnr_strerror.argtypes = [ctypes.c_int]
         L.qkvnr_strerror.restype = ctypes.c_char_p
         L.qkvnr_version.argtypes = []
@@ -199,6 +202,14 @@ def qkvnr_ns_poly(dtype: int, blocks: int, d: int, gram, parts: int, first: bool
     """Call ``qkvnr_ns_poly``."""
     _check(lib().qkvnr_ns_poly(dtype, blocks, d, _ptr(gram), parts, 1 if first else 0, scale, eps, _ptr(p),
                                _stream(stream)))
+
+
+def qkvnr_proj_forward(layout: Layout, hidden: int, x, w_qkv, positions, q_norm_w, k_norm_w, eps: float,
+                       theta: float, q, k, v, stream=None) -> None:
+    """Call ``qkvnr_proj_forward``."""
+    _check(lib().qkvnr_proj_forward(ctypes.byref(layout), hidden, _ptr(x), _ptr(w_qkv), _ptr(positions),
+                                    _ptr(q_norm_w), _ptr(k_norm_w), eps, theta, _ptr(q), _ptr(k), _ptr(v),
+                                    _stream(stream)))
 
 
 def qkvnr_version() -> int:
@@ -314,3 +325,31 @@ def rope_inplace(x: torch.Tensor, positions: torch.Tensor, *, rope_offset: int, 
     qkvnr_rope_inplace(DTYPES[x.dtype], x.shape[0], x.shape[1], x.stride(0), x.stride(1), rope_offset, rope_dim,
                        positions, theta, x, stream)
     return x
+
+
+def proj_forward(x: torch.Tensor, w_qkv: torch.Tensor, positions: Optional[torch.Tensor], q_norm_w: torch.Tensor,
+                 k_norm_w: torch.Tensor, *, kind: str, n_kv: int, q_per_kv: int, head_dim: int, rope: bool = True,
+                 eps: float = 1e-6, theta: float = 10000.0,
+                 out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None, stream=None):
+    """The QKV projection x w_qkv^T with split + q/k RMSNorm + RoPE in its epilogue (bf16).
+
+    x [T, hidden] and w_qkv [(n_q + 2 n_kv) * head_dim, hidden] are contiguous;
+    the weight's head blocks are in the ``kind`` order.  Returns contiguous
+    (q [T, n_q, D], k [T, n_kv, D], v [T, n_kv, D]).
+    """
+    if x.dim() != 2 or w_qkv.dim() != 2 or not x.is_contiguous() or not w_qkv.is_contiguous():
+        raise ValueError("x and w_qkv must be contiguous 2-D tensors")
+    T, hidden = x.shape
+    width = (n_kv * q_per_kv + 2 * n_kv) * head_dim
+    if w_qkv.shape[1] != hidden:
+        raise ValueError(f"w_qkv has {w_qkv.shape[1]} columns, x has {hidden}")
+    L = Layout(kind=KINDS[kind], dtype=DTYPES[x.dtype], T=T, n_kv=n_kv, q_per_kv=q_per_kv, head_dim=head_dim,
+               rope_dim=head_dim if rope else 0, norm_dim=0, reserved=0, width=w_qkv.shape[0], in_row_stride=width)
+    if out is None:
+        q = torch.empty((T, n_kv * q_per_kv, head_dim), dtype=x.dtype, device=x.device)
+        k = torch.empty((T, n_kv, head_dim), dtype=x.dtype, device=x.device)
+        v = torch.empty((T, n_kv, head_dim), dtype=x.dtype, device=x.device)
+    else:
+        q, k, v = out
+    qkvnr_proj_forward(L, hidden, x, w_qkv, positions, q_norm_w, k_norm_w, eps, theta, q, k, v, stream)
+    return q, k, v

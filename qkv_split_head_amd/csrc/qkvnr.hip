@@ -10,6 +10,7 @@
 
 #include "kernels.h"
 #include "muon.h"
+#include "proj.h"
 #include "qkvnr.h"
 
 namespace {
@@ -568,6 +569,74 @@ int qkvnr_ns_poly(int32_t dtype, int64_t blocks, int32_t d, float* gram, int32_t
     else hipLaunchKernelGGL((ns_poly_kernel<float, 0>), grid, dim3(kNsThreads), 0, stream, gram, o, d, parts, fi, scale, eps);
   }
   return launched("Newton-Schulz polynomial");
+}
+
+int qkvnr_proj_forward(const qkvnr_layout* layout, int64_t hidden, const void* x, const void* w_qkv,
+                       const int32_t* positions, const void* q_norm_w, const void* k_norm_w, float eps,
+                       double theta, void* q, void* k, void* v, hipStream_t stream) {
+  if (int rc = check_layout(layout)) return rc;
+  const qkvnr_layout* L = layout;
+  if (L->kind == QKVNR_LATENT) return fail(QKVNR_EUNSUPPORTED, "the fused projection has no latent kernel");
+  if (L->dtype != QKVNR_BF16) return fail(QKVNR_EUNSUPPORTED, "the fused projection is bf16 only");
+  if (int rc = check_scalars(L, eps, theta)) return rc;
+  if (hidden < kProjBK || hidden % kProjBK || hidden > (1 << 30))
+    return fail(QKVNR_EINVAL, "hidden %lld must be a positive multiple of %d, at most 2^30", (long long)hidden,
+                kProjBK);
+  if (L->width > INT32_MAX) return fail(QKVNR_EINVAL, "width %lld above 2^31", (long long)L->width);
+  if (L->T == 0) return QKVNR_OK;  // nothing is read or written
+  const bool rope = L->rope_dim > 0;
+  if (int rc = need16(x, "x")) return rc;
+  if (int rc = need16(w_qkv, "w_qkv")) return rc;
+  if (rope) {
+    if (int rc = need4(positions, "positions")) return rc;
+  }
+  if (int rc = need16(q_norm_w, "q_norm_w")) return rc;
+  if (int rc = need16(k_norm_w, "k_norm_w")) return rc;
+  if (int rc = need16(q, "q")) return rc;
+  if (int rc = need16(k, "k")) return rc;
+  if (int rc = need16(v, "v")) return rc;
+  const int64_t D = L->head_dim, n_q = static_cast<int64_t>(L->n_kv) * L->q_per_kv;
+  const int64_t kv_bytes = L->T * L->n_kv * D * 2;
+  if (int rc = check_disjoint({{q, L->T * n_q * D * 2}, {k, kv_bytes}, {v, kv_bytes}},
+                              {{x, L->T * hidden * 2},
+                               {w_qkv, L->width * hidden * 2},
+                               {positions, rope ? L->T * 4 : 0},
+                               {q_norm_w, D * 2},
+                               {k_norm_w, D * 2}}))
+    return rc;
+  const int64_t tiles_m = (L->T + kProjBM - 1) / kProjBM, tiles_n = (L->width + kProjBN - 1) / kProjBN;
+  if (tiles_m * tiles_n > INT32_MAX) return fail(QKVNR_EINVAL, "T %lld: too many tiles for one launch", (long long)L->T);
+  int cus = 0;
+  if (int rc = current_device(&cus)) return rc;
+  ProjArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.w = static_cast<const uint16_t*>(w_qkv);
+  a.pos = positions;
+  a.wq = static_cast<const uint16_t*>(q_norm_w);
+  a.wk = static_cast<const uint16_t*>(k_norm_w);
+  a.q = static_cast<uint16_t*>(q);
+  a.k = static_cast<uint16_t*>(k);
+  a.v = static_cast<uint16_t*>(v);
+  a.T = L->T;
+  a.hidden = static_cast<int32_t>(hidden);
+  a.width = static_cast<int32_t>(L->width);
+  a.tiles_n = static_cast<int32_t>(tiles_n);
+  a.kind = L->kind == QKVNR_INTERLEAVED ? 0 : 1;
+  a.n_kv = L->n_kv;
+  a.q_per_kv = L->q_per_kv;
+  a.n_q = static_cast<int32_t>(n_q);
+  a.heads = static_cast<int32_t>(n_q + 2 * L->n_kv);
+  a.eps = eps;
+  if (rope) fill_turns(a.turns, theta, L->rope_dim);
+  const dim3 grid(static_cast<uint32_t>(tiles_m * tiles_n)), block(kProjThreads);
+  if (D == 128) {
+    if (rope) hipLaunchKernelGGL((proj_qkv_kernel<128, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((proj_qkv_kernel<128, false>), grid, block, 0, stream, a);
+  } else {
+    if (rope) hipLaunchKernelGGL((proj_qkv_kernel<64, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((proj_qkv_kernel<64, false>), grid, block, 0, stream, a);
+  }
+  return launched("fused projection");
 }
 
 const char* qkvnr_strerror(int code) {

@@ -301,3 +301,31 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(b, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="no fallback"):
         b.lib()
+
+
+def test_proj_forward_argument_checks():
+    f = qk.lib().qkvnr_proj_forward
+
+    def call(L=None, hidden=4096, x=A, w=B, pos=C, wq=C + 4096, wk=C + 8192, q=Dp, k=E, v=F, eps=1e-6, theta=1e6):
+        L = _lay(qk.SECTIONED, T=300, n_kv=8, q_per_kv=4, head_dim=128, rope_dim=128) if L is None else L
+        return f(ctypes.byref(L), hidden, x, w, pos, wq, wk, eps, theta, q, k, v, None)
+
+    assert call(hidden=4100) == qk.EINVAL                     # not a multiple of 64
+    assert call(hidden=0) == qk.EINVAL
+    assert call(hidden=(1 << 30) + 64) == qk.EINVAL
+    assert call(L=_lay(qk.LATENT, T=4, width=576, norm_dim=512, rope_dim=64)) == qk.EUNSUPPORTED
+    assert call(L=_lay(qk.SECTIONED, dtype=qk.FP32, T=4, n_kv=8, q_per_kv=4, head_dim=128, rope_dim=128)) \
+        == qk.EUNSUPPORTED
+    assert call(L=_lay(qk.SECTIONED, T=4, n_kv=8, q_per_kv=4, head_dim=128, rope_dim=128, width=6016)) == qk.EINVAL
+    assert call(L=_lay(qk.SECTIONED, T=4, n_kv=8, q_per_kv=4, head_dim=96, rope_dim=96)) == qk.EUNSUPPORTED
+    assert call(x=A + 8) == qk.EALIGN
+    assert call(w=B + 2) == qk.EALIGN
+    assert call(pos=C + 2) == qk.EALIGN
+    assert call(q=None) == qk.EINVAL
+    assert call(v=A + 64) == qk.EINVAL                          # an output overlaps x
+    assert call(k=B + 4096) == qk.EINVAL                        # an output overlaps the weight
+    assert call(eps=-1.0) == qk.EINVAL
+    assert call(theta=0.0) == qk.EINVAL
+    # NoPE: positions may be NULL (the call then fails only for want of a device here)
+    nope = _lay(qk.INTERLEAVED, T=0, n_kv=2, q_per_kv=4, head_dim=64, rope_dim=0)
+    assert call(L=nope, pos=None, x=0, w=0, q=0, k=0, v=0) == qk.OK   # T == 0 enqueues nothing
