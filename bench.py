@@ -204,6 +204,57 @@ def muon_extras(stream, n: int = 10):
     return out
 
 
+def proj_extras(stream, n: int = 20):
+    """The QKV projection of the Qwen3-8B-like training layer (x [16384, 4096] @ w_qkv[6144, 4096]^T, bf16)
+    with split + q/k RMSNorm + RoPE fused into its epilogue, against the library GEMM followed by the
+    region's forward, and the library GEMM alone.  MFMA-bound: 2 T hidden width flops."""
+    import torch
+    import torch.nn.functional as F
+    import qkv_split_head_amd as qk
+
+    T, H, n_kv, Q, D = 16384, 4096, 8, 4, 128
+    W = (n_kv * Q + 2 * n_kv) * D
+    g = torch.Generator(device="cuda").manual_seed(81)
+    x = torch.randn((T, H), generator=g, device="cuda").to(torch.bfloat16)
+    w = (torch.randn((W, H), generator=g, device="cuda") * H ** -0.5).to(torch.bfloat16)
+    pos = torch.arange(T, dtype=torch.int32, device="cuda")
+    wq = (1.0 + 0.1 * torch.randn(D, generator=g, device="cuda")).to(torch.bfloat16)
+    wk = (1.0 + 0.1 * torch.randn(D, generator=g, device="cuda")).to(torch.bfloat16)
+    shapes = ((T, n_kv * Q, D), (T, n_kv, D), (T, n_kv, D))
+    out = tuple(torch.empty(sh, dtype=torch.bfloat16, device="cuda") for sh in shapes)
+    out2 = tuple(torch.empty(sh, dtype=torch.bfloat16, device="cuda") for sh in shapes)
+    kw = dict(kind="sectioned", n_kv=n_kv, q_per_kv=Q, head_dim=D, theta=1e6)
+
+    def fused():
+        qk.proj_forward(x, w, pos, wq, wk, out=out, stream=stream, **kw)
+
+    def unfused():
+        qk.forward(F.linear(x, w), pos, wq, wk, out=out2, stream=stream, **kw)
+
+    def gemm():
+        F.linear(x, w)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return round(e0.elapsed_time(e1) / n * 1e3, 1)
+
+    res = {"shape": [T, H, W], "fused_us": timed(fused), "gemm_then_region_us": timed(unfused),
+           "gemm_alone_us": timed(gemm)}
+    flops = 2 * T * H * W
+    res["fused_TFLOPs"] = round(flops / (res["fused_us"] * 1e-6) / 1e12, 1)
+    res["fused_frac_of_bf16_mfma_peak"] = round(flops / (res["fused_us"] * 1e-6) / 2.5e15, 3)
+    res["gemm_alone_TFLOPs"] = round(flops / (res["gemm_alone_us"] * 1e-6) / 1e12, 1)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -407,6 +458,9 @@ def main():
 
         # ------------------------------------------------------------ per-head Newton-Schulz on the fused weight
         extras["muon_newton_schulz"] = muon_extras(stream)
+
+        # ------------------------------------------------------------ QKV projection with the region in its epilogue
+        extras["fused_qkv_projection"] = proj_extras(stream)
 
     out = {
         "metric": METRIC,

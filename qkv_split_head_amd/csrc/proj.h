@@ -13,13 +13,16 @@
 // The product is a plain NT GEMM: x [T, hidden] and w_qkv [width, hidden] are
 // both read along hidden.  Workgroup tile: 256 tokens x 256 packed columns (2
 // heads of 128 or 4 of 64, so every head of the tile is whole), hidden in steps
-// of 64, two LDS stages of 2 x 32 KB.  Four waves of 128 x 128.  The products
-// are taken transposed, C^T = w x^T (v_mfma_f32_32x32x16_bf16 with the weight
-// rows as the first operand): register e of lane l then holds packed column
-// 8 (e / 4) + 4 (l / 32) + e % 4 of its 32-column tile for token l mod 32, so a
-// lane owns 4 adjacent values of a head for each of its tokens.  A head's sum of
-// squares is the lane's own sum plus one exchange with lane l ^ 32, and the
-// rotate-half partner of a value is in the same lane, 64 (or 32) columns on.
+// of 64, two LDS stages of 2 x 32 KB filled from registers one step ahead.  Four
+// waves of 128 x 128; the products are taken transposed, C^T = w x^T
+// (v_mfma_f32_32x32x16_bf16 with the weight rows as the first operand), and the
+// LDS reads, LDS stores and global loads of a step are spread one by one between
+// its MFMAs.  Workgroups are persistent (one per CU) and take the tiles in a
+// grouped order that keeps the tiles one XCD runs at once on shared rows.
+// The epilogue moves each half of the tile to LDS as fp32 and finishes it the
+// way the region's forward does: D / 16 threads per token head, a lane-group sum
+// of squares, cos / sin of each thread's rotate-half pairs shared by the token's
+// heads, and 16-byte stores of q, k and v.
 #pragma once
 
 #include "device.h"
@@ -31,6 +34,8 @@ typedef float pf32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kProjBM = 256, kProjBN = 256, kProjBK = 64;
 constexpr int kProjThreads = 256;
+constexpr int kProjGroupM = 4;  // token tiles per group of the tile order
+static_assert(kProjThreads == kProjBM, "one thread per token of a tile fills the position table");
 constexpr int kProjMaxPairs = 64;
 
 struct ProjArgs {
@@ -46,6 +51,7 @@ struct ProjArgs {
   int32_t hidden;
   int32_t width;         // (n_q + 2 n_kv) D
   int32_t tiles_n;       // ceil(width / 256)
+  int32_t tiles_m;       // ceil(T / 256)
   int32_t kind;          // 0 interleaved, 1 sectioned
   int32_t n_kv;
   int32_t q_per_kv;
@@ -54,6 +60,19 @@ struct ProjArgs {
   float eps;
   double turns[kProjMaxPairs];  // turns per position of rotate-half pair i: theta^(-2i/R) / (2 pi)
 };
+
+__device__ __forceinline__ float proj_bf16_f32(uint16_t b) { return __builtin_bit_cast(float, static_cast<uint32_t>(b) << 16); }
+
+// Sum over an aligned group of G lanes (G = 4 or 8); every lane of the group gets the same bits.
+template <int G>
+__device__ __forceinline__ float proj_group_sum(float v) {
+  if constexpr (G == 4) {
+    v += dpp<kQuadXor1>(v);
+    return v + dpp<kQuadXor2>(v);
+  } else {
+    return head_sum<G>(v);
+  }
+}
 
 // Which output a packed head block is: type 0 = q, 1 = k, 2 = v, and its head index there.
 __device__ __forceinline__ void proj_head(const ProjArgs& a, int h, int& type, int& idx) {
@@ -73,33 +92,48 @@ __global__ __launch_bounds__(kProjThreads, 1) void proj_qkv_kernel(const ProjArg
   constexpr int ROWS = kProjBM * PIECES;    // pieces of one operand tile
   constexpr int PER = kProjBM / (kProjThreads / PIECES);  // rows each thread loads per operand (8)
   __shared__ uint4 lds[2][2][ROWS];         // [stage][x, w][row * 8 + swizzled piece]: 128 KB
+  __shared__ uint16_t ep_w[2][D];           // q and k norm weights, for the epilogue
+  __shared__ double ep_turns[D / 2];        // turns per position of each rotate-half pair
+  __shared__ int32_t ep_pos[kProjBM];       // positions of the current tile's tokens
+  if (threadIdx.x < D) {
+    ep_w[0][threadIdx.x] = a.wq[threadIdx.x];
+    ep_w[1][threadIdx.x] = a.wk[threadIdx.x];
+    if (ROPE && threadIdx.x < D / 2) ep_turns[threadIdx.x] = a.turns[threadIdx.x];
+  }
   const int lane = threadIdx.x & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int wm = w >> 1, wn = w & 1;
-  const int tn = blockIdx.x % a.tiles_n;
-  const int64_t tm = blockIdx.x / a.tiles_n;
-  const int64_t m0 = tm * kProjBM;
-  const int n0 = tn * kProjBN;
+
+  // ---- persistent workgroups walk the tiles in rounds of gridDim.x.  Workgroup b runs on XCD
+  // b mod 8, and in each round the XCD's workgroups take consecutive tiles of a grouped order
+  // (kProjGroupM token tiles by every head tile), so the ones an XCD runs at once share operand
+  // rows in its L2.
+  const int P = gridDim.x;
+  const int tiles = a.tiles_m * a.tiles_n;
+  const int slot_in_round = P % 8 == 0 ? (blockIdx.x % 8) * (P / 8) + blockIdx.x / 8 : blockIdx.x;
+  auto tile_of = [&](int L, int64_t& m0, int& n0) {
+    const int group = L / (kProjGroupM * a.tiles_n), within = L % (kProjGroupM * a.tiles_n);
+    const int gm = min(kProjGroupM, a.tiles_m - group * kProjGroupM);
+    m0 = static_cast<int64_t>(group * kProjGroupM + within % gm) * kProjBM;
+    n0 = (within / gm) * kProjBN;
+  };
 
   // ---- operand loads: thread t loads piece t mod 8 of rows t / 8 + 32 j (rows past the end clamped)
   const int q = threadIdx.x % PIECES;
-  const uint16_t* pa[PER];
-  const uint16_t* pb[PER];
   int slot[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const int r = threadIdx.x / PIECES + (kProjThreads / PIECES) * j;
-    pa[j] = a.x + min<int64_t>(m0 + r, a.T - 1) * a.hidden + 8 * q;
-    pb[j] = a.w + static_cast<int64_t>(min(n0 + r, a.width - 1)) * a.hidden + 8 * q;
     slot[j] = r * PIECES + (q ^ ((r >> 1) & 7));  // the 16 rows one operand read serves hit every bank once
   }
   uint4 sa[PER], sb[PER];
-  auto gload = [&](int kt) {
-    const int off = kt * kProjBK;
+  auto gload = [&](int64_t gm0, int gn0, int kt) {
+    const int off = kt * kProjBK + 8 * q;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-      sa[j] = ld16(pa[j] + off);
-      sb[j] = ld16(pb[j] + off);
+      const int r = threadIdx.x / PIECES + (kProjThreads / PIECES) * j;
+      sa[j] = ld16(a.x + min<int64_t>(gm0 + r, a.T - 1) * a.hidden + off);
+      sb[j] = ld16(a.w + static_cast<int64_t>(min(gn0 + r, a.width - 1)) * a.hidden + off);
     }
   };
   auto lstore = [&](int stage) {
@@ -118,10 +152,6 @@ __global__ __launch_bounds__(kProjThreads, 1) void proj_qkv_kernel(const ProjArg
   // ---- MFMA fragments: step s of a K step, lane l reads piece 2 s + l / 32 of row l mod 32 of a 32-row group
   const int rr = lane % 32, h = lane / 32, sw = (rr >> 1) & 7;
   pf32x16_t acc[4][4];  // [packed 32-column tile j][token tile i]
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[j][i] = pf32x16_t{};
   uint4 fa[2][4], fb[2][4];
   auto reads = [&](int stage, int s, uint4 (&xa)[4], uint4 (&xb)[4]) {
     const int pos = (2 * s + h) ^ sw;
@@ -138,136 +168,173 @@ __global__ __launch_bounds__(kProjThreads, 1) void proj_qkv_kernel(const ProjArg
         acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(pbf16x8_t, xb[j]),
                                                             __builtin_bit_cast(pbf16x8_t, xa[i]), acc[j][i], 0, 0, 0);
   };
+  // Instruction order inside a K step, one MFMA at a time with the other work between them (the
+  // scheduler is told the pattern, so no burst of reads or stores stalls the matrix unit):
+  //   steps 0-2: 16 MFMAs, the 8 fragment reads of the next step between the first 8
+  //   step 3: 16 MFMAs, with the 16 LDS stores of the next K step and the 16 global loads of the
+  //           K step after next (each load after the store that frees its registers) between
+  //           them; then the barrier and the reads of the next K step's step 0
+  auto interleave = [](int reads, int writes, int vloads) {
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // one MFMA
+      if (m < reads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      if (m < writes) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0); // one LDS write
+      if (m < vloads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); // one global load
+    }
+  };
 
+  constexpr int HEADS = kProjBN / D;          // heads per tile row
+  constexpr int G = D / 16;                   // threads per token
+  constexpr int TOK_PER_PASS = kProjThreads / G;
+  const int k = threadIdx.x % G;
   const int KT = a.hidden / kProjBK;
-  gload(0);
-  lstore(0);
-  gload(min(1, KT - 1));
-  lds_barrier();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int stage = kt & 1;
-    // step kt + 1 goes to the other stage (last read before the previous barrier) during this step's
-    // products; the load of step kt + 2 follows it (past the end it reloads the last step, unused)
-    reads(stage, 0, fa[0], fb[0]);
-    __builtin_amdgcn_sched_barrier(0);
-    reads(stage, 1, fa[1], fb[1]);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(fa[0], fb[0]);
-    __builtin_amdgcn_sched_barrier(0);
-    lstore(stage ^ 1);
-    gload(min(kt + 2, KT - 1));
-    __builtin_amdgcn_sched_barrier(0);
-    reads(stage, 2, fa[0], fb[0]);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(fa[1], fb[1]);
-    __builtin_amdgcn_sched_barrier(0);
-    reads(stage, 3, fa[1], fb[1]);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(fa[0], fb[0]);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(fa[1], fb[1]);
-    __builtin_amdgcn_sched_barrier(0);
-    lds_barrier();
+  int L = slot_in_round;
+  int64_t m0 = 0, nm0 = 0;
+  int n0 = 0, nn0 = 0;
+  if (L < tiles) {
+    tile_of(L, m0, n0);
+    gload(m0, n0, 0);  // the first tile's first K step
   }
-
-  // ---- epilogue.  Lane (rr, h) holds, for token 128 wm + 32 i + rr and packed tile j, the columns
-  // 128 wn + 32 j + 8 c + 4 h + r in register 4 c + r.  A head is D / 32 consecutive tiles j.
-  constexpr int TPH = D / 32;              // tiles per head
-  constexpr int HPW = 4 / TPH;             // heads per wave
-  const int hb0 = (n0 + 128 * wn) / D;     // first packed head of this wave
-  float wv[HPW][TPH][16];                  // norm weight of each held column (per head type)
-  int type[HPW], idx[HPW];
-#pragma unroll
-  for (int hh = 0; hh < HPW; ++hh) {
-    proj_head(a, min(hb0 + hh, a.heads - 1), type[hh], idx[hh]);
-    const uint16_t* wsrc = type[hh] == 0 ? a.wq : a.wk;
-#pragma unroll
-    for (int jj = 0; jj < TPH; ++jj)
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        wv[hh][jj][e] = type[hh] == 2 ? 1.0f
-                                      : __builtin_bit_cast(float, static_cast<uint32_t>(wsrc[32 * jj + 8 * (e / 4) + 4 * h + e % 4]) << 16);
-  }
-  const float inv_d = 1.0f / D;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t t = m0 + 128 * wm + 32 * i + rr;
-    float ss[HPW];
-#pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) {
-      float s = 0.0f;
-#pragma unroll
-      for (int jj = 0; jj < TPH; ++jj)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s = fmaf(acc[hh * TPH + jj][i][e], acc[hh * TPH + jj][i][e], s);
-      ss[hh] = s + __shfl_xor(s, 32, kWave);  // the other half of the head's columns
-    }
-    if constexpr (ROPE) {
-      // cos / sin of pair p = 32 jj + 8 c + 4 h + r (jj < TPH / 2) at this token's position
-      const int32_t p = a.pos[min<int64_t>(t, a.T - 1)];
-      float cs[TPH / 2][16], sn[TPH / 2][16];
-#pragma unroll
-      for (int jj = 0; jj < TPH / 2; ++jj)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) rope_cos_sin(p, a.turns[32 * jj + 8 * (e / 4) + 4 * h + e % 4], cs[jj][e], sn[jj][e]);
-#pragma unroll
-      for (int hh = 0; hh < HPW; ++hh) {
-        if (type[hh] == 2) continue;
-        const float r = rsqrtf(fmaf(ss[hh], inv_d, a.eps));
-#pragma unroll
-        for (int jj = 0; jj < TPH / 2; ++jj)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const float nl = acc[hh * TPH + jj][i][e] * r * wv[hh][jj][e];
-            const float nh = acc[hh * TPH + jj + TPH / 2][i][e] * r * wv[hh][jj + TPH / 2][e];
-            acc[hh * TPH + jj][i][e] = nl * cs[jj][e] - nh * sn[jj][e];
-            acc[hh * TPH + jj + TPH / 2][i][e] = nh * cs[jj][e] + nl * sn[jj][e];
-          }
-      }
-    } else {
-#pragma unroll
-      for (int hh = 0; hh < HPW; ++hh) {
-        if (type[hh] == 2) continue;
-        const float r = rsqrtf(fmaf(ss[hh], inv_d, a.eps));
-#pragma unroll
-        for (int jj = 0; jj < TPH; ++jj)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc[hh * TPH + jj][i][e] = acc[hh * TPH + jj][i][e] * r * wv[hh][jj][e];
-      }
-    }
-  }
-
-  // ---- bf16 tile through LDS (the operand stages are free after the last barrier), then rows out.
-  // Staging row = token of the tile, 32 granules of 16 bytes; granule g of row r sits at g ^ (r mod 32).
-  uint4* st = &lds[0][0][0];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 128 * wm + 32 * i + rr;
+  __syncthreads();     // the epilogue tables above are complete
+  for (; L < tiles; L += P) {
+    const int Ln = L + P;  // the next tile of this workgroup, whose first K step loads during this one's last
+    if (Ln < tiles) tile_of(Ln, nm0, nn0);
+    if (ROPE) ep_pos[threadIdx.x] = a.pos[min<int64_t>(m0 + threadIdx.x, a.T - 1)];  // kProjThreads == kProjBM
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int g = 16 * wn + 4 * j + c;
-        uint2* dst = reinterpret_cast<uint2*>(st + row * 32 + (g ^ (row & 31))) + h;
-        *dst = make_uint2(pack_bf16x2(acc[j][i][4 * c], acc[j][i][4 * c + 1]),
-                          pack_bf16x2(acc[j][i][4 * c + 2], acc[j][i][4 * c + 3]));
-      }
-  }
-  __syncthreads();
-  // 256 rows x 32 granules; thread t takes granule t mod 32 of rows t / 32 + 8 u
-#pragma unroll 4
-  for (int u = 0; u < kProjBM / 8; ++u) {
-    const int row = threadIdx.x / 32 + 8 * u, g = threadIdx.x % 32;
-    const int64_t t = m0 + row;
-    const int col = n0 + 8 * g;            // packed column of the granule
-    const int hb = col / D;
-    if (t < a.T && hb < a.heads) {
-      int ty, ix;
-      proj_head(a, hb, ty, ix);
-      uint16_t* base = ty == 0 ? a.q : (ty == 1 ? a.k : a.v);
-      const int nh = ty == 0 ? a.n_q : a.n_kv;
-      st16(base + (t * nh + ix) * D + col % D, st[row * 32 + (g ^ (row & 31))]);
+      for (int i = 0; i < 4; ++i) acc[j][i] = pf32x16_t{};
+    lstore(0);
+    gload(m0, n0, min(1, KT - 1));
+    lds_barrier();
+    reads(0, 0, fa[0], fb[0]);
+    for (int kt = 0; kt < KT; ++kt) {
+      const int stage = kt & 1;
+      __builtin_amdgcn_sched_barrier(0);
+      reads(stage, 1, fa[1], fb[1]);
+      mfmas(fa[0], fb[0]);
+      interleave(8, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      reads(stage, 2, fa[0], fb[0]);
+      mfmas(fa[1], fb[1]);
+      interleave(8, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      reads(stage, 3, fa[1], fb[1]);
+      mfmas(fa[0], fb[0]);
+      interleave(8, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      // step kt + 1 goes to the other stage (last read before the previous barrier), then the loads
+      // of step kt + 2, or in the last two steps those of the next tile's first step (which waits in
+      // the registers through this tile's epilogue; without a next tile, the last step again).  The
+      // same work on every step keeps the loop free of branches; what the last step stores is unused.
+      const bool here = kt + 2 < KT, next = Ln < tiles;
+      const int64_t gm = here || !next ? m0 : nm0;
+      const int gn = here || !next ? n0 : nn0;
+      const int gk = here ? kt + 2 : (next ? 0 : KT - 1);
+      lstore(stage ^ 1);
+      gload(gm, gn, gk);
+      mfmas(fa[1], fb[1]);
+      interleave(0, 16, 16);
+      __builtin_amdgcn_sched_barrier(0);
+      lds_barrier();
+      reads(stage ^ 1, 0, fa[0], fb[0]);  // past the last step: unused
     }
+
+    // ---- epilogue, one half of the tile's tokens at a time (the operand stages are free after the
+    // last barrier).  Lane (rr, h) of wave (wm, wn) holds, for token 128 wm + 32 i + rr and packed tile
+    // j, the columns 128 wn + 32 j + 8 c + 4 h + r in register 4 c + r.  Half hf takes the token tiles
+    // i = 2 hf, 2 hf + 1 of both wm: its 128 tokens go to LDS as fp32 rows of the tile's 256 columns
+    // (local row 64 wm + 32 (i - 2 hf) + rr; 16-byte granule g of row r at g ^ (r mod 16)).  Then each
+    // token's heads are taken by G = D / 16 adjacent threads, thread k owning the columns
+    // [8 k, 8 k + 8) of a head and their rotate-half partners [D/2 + 8 k, D/2 + 8 k + 8): the sum of
+    // squares is a reduction over the G lanes, and cos / sin of the thread's 8 pairs serve every head
+    // of the token.
+    float* ep = reinterpret_cast<float*>(&lds[0][0][0]);  // [128][256] fp32, swizzled granules
+    // the q and k weights of the thread's 16 columns, as fp32 (the same for every token)
+    float wqv[16], wkv[16];
+  #pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      wqv[c] = proj_bf16_f32(ep_w[0][8 * k + c]);
+      wqv[8 + c] = proj_bf16_f32(ep_w[0][D / 2 + 8 * k + c]);
+      wkv[c] = proj_bf16_f32(ep_w[1][8 * k + c]);
+      wkv[8 + c] = proj_bf16_f32(ep_w[1][D / 2 + 8 * k + c]);
+    }
+    const float inv_d = 1.0f / D;
+  #pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+  #pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+        const int i = 2 * hf + ii, lr = 64 * wm + 32 * ii + rr;
+  #pragma unroll
+        for (int j = 0; j < 4; ++j)
+  #pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int g = 32 * wn + 8 * j + 2 * c + h;
+            *reinterpret_cast<float4*>(ep + lr * kProjBN + 4 * (g ^ (lr & 15))) =
+                make_float4(acc[j][i][4 * c], acc[j][i][4 * c + 1], acc[j][i][4 * c + 2], acc[j][i][4 * c + 3]);
+          }
+      }
+      __syncthreads();
+  #pragma unroll 1
+      for (int lr = threadIdx.x / G; lr < 128; lr += TOK_PER_PASS) {
+        const int64_t t = m0 + 128 * (lr / 64) + 64 * hf + lr % 64;
+        float cs[8], sn[8];
+        if constexpr (ROPE) {
+          const int32_t p = ep_pos[128 * (lr / 64) + 64 * hf + lr % 64];
+  #pragma unroll
+          for (int c = 0; c < 8; ++c) rope_cos_sin(p, ep_turns[8 * k + c], cs[c], sn[c]);
+        }
+        const float* rowp = ep + lr * kProjBN;
+  #pragma unroll
+        for (int hd = 0; hd < HEADS; ++hd) {
+          const int hb = (n0 + hd * D) / D;
+          int ty, ix;
+          proj_head(a, min(hb, a.heads - 1), ty, ix);
+          float lo[8], hi[8];
+          {
+            const int g0 = (hd * D + 8 * k) / 4, g1 = (hd * D + D / 2 + 8 * k) / 4;
+            const float4 l0 = *reinterpret_cast<const float4*>(rowp + 4 * (g0 ^ (lr & 15)));
+            const float4 l1 = *reinterpret_cast<const float4*>(rowp + 4 * ((g0 + 1) ^ (lr & 15)));
+            const float4 h0 = *reinterpret_cast<const float4*>(rowp + 4 * (g1 ^ (lr & 15)));
+            const float4 h1 = *reinterpret_cast<const float4*>(rowp + 4 * ((g1 + 1) ^ (lr & 15)));
+            lo[0] = l0.x; lo[1] = l0.y; lo[2] = l0.z; lo[3] = l0.w; lo[4] = l1.x; lo[5] = l1.y; lo[6] = l1.z; lo[7] = l1.w;
+            hi[0] = h0.x; hi[1] = h0.y; hi[2] = h0.z; hi[3] = h0.w; hi[4] = h1.x; hi[5] = h1.y; hi[6] = h1.z; hi[7] = h1.w;
+          }
+          if (ty != 2) {
+            float ssq = 0.0f;
+  #pragma unroll
+            for (int c = 0; c < 8; ++c) ssq = fmaf(lo[c], lo[c], fmaf(hi[c], hi[c], ssq));
+            ssq = proj_group_sum<G>(ssq);
+            const float r = rsqrtf(fmaf(ssq, inv_d, a.eps));
+            const float* wv = ty == 0 ? wqv : wkv;
+  #pragma unroll
+            for (int c = 0; c < 8; ++c) {
+              const float nl = lo[c] * r * wv[c], nh = hi[c] * r * wv[8 + c];
+              if constexpr (ROPE) {
+                lo[c] = nl * cs[c] - nh * sn[c];
+                hi[c] = nh * cs[c] + nl * sn[c];
+              } else {
+                lo[c] = nl;
+                hi[c] = nh;
+              }
+            }
+          }
+          if (t < a.T && hb < a.heads) {
+            uint16_t* base = ty == 0 ? a.q : (ty == 1 ? a.k : a.v);
+            const int nh = ty == 0 ? a.n_q : a.n_kv;
+            uint16_t* dst = base + (t * nh + ix) * D + 8 * k;
+            st16(dst, make_uint4(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(lo[4], lo[5]),
+                                 pack_bf16x2(lo[6], lo[7])));
+            st16(dst + D / 2, make_uint4(pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3]),
+                                         pack_bf16x2(hi[4], hi[5]), pack_bf16x2(hi[6], hi[7])));
+          }
+        }
+      }
+      __syncthreads();
+    }
+    m0 = nm0;
+    n0 = nn0;
   }
 }
 

@@ -2,6 +2,7 @@
 //
 // Every check runs on the host before the first HIP call, so a rejected call
 // enqueues nothing and the checks can be exercised on a machine with no GPU.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -621,6 +622,7 @@ int qkvnr_proj_forward(const qkvnr_layout* layout, int64_t hidden, const void* x
   a.hidden = static_cast<int32_t>(hidden);
   a.width = static_cast<int32_t>(L->width);
   a.tiles_n = static_cast<int32_t>(tiles_n);
+  a.tiles_m = static_cast<int32_t>(tiles_m);
   a.kind = L->kind == QKVNR_INTERLEAVED ? 0 : 1;
   a.n_kv = L->n_kv;
   a.q_per_kv = L->q_per_kv;
@@ -628,7 +630,8 @@ int qkvnr_proj_forward(const qkvnr_layout* layout, int64_t hidden, const void* x
   a.heads = static_cast<int32_t>(n_q + 2 * L->n_kv);
   a.eps = eps;
   if (rope) fill_turns(a.turns, theta, L->rope_dim);
-  const dim3 grid(static_cast<uint32_t>(tiles_m * tiles_n)), block(kProjThreads);
+  // persistent workgroups, one per CU (each holds 130 KB of LDS), or one per tile when there are fewer
+  const dim3 grid(static_cast<uint32_t>(std::min<int64_t>(tiles_m * tiles_n, cus))), block(kProjThreads);
   if (D == 128) {
     if (rope) hipLaunchKernelGGL((proj_qkv_kernel<128, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((proj_qkv_kernel<128, false>), grid, block, 0, stream, a);

@@ -73,6 +73,9 @@ CASES = [
     ("sectioned", 100, 128, 1, 1, 128, True, "arange"),     # 3 heads of 128: the second head tile holds one
     ("sectioned", 513, 512, 8, 4, 128, True, "random"),
     ("interleaved", 1, 64, 16, 8, 64, True, "random"),      # one token (decode-like)
+    # 8 x 40 = 320 tiles: more than one per persistent workgroup on a 256-CU part, ragged last token tile
+    ("interleaved", 2000, 256, 16, 8, 64, True, "random"),
+    ("sectioned", 700, 64, 8, 4, 128, False, "arange"),     # one K step per tile, several tiles per workgroup
 ]
 
 
