@@ -182,7 +182,7 @@ def muon_extras(stream, n: int = 10):
         return X.t() * (6144 / 4096) ** 0.5
 
     def timed(fn):
-        for _ in range(2):
+        for _ in range(5):
             fn()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -235,7 +235,7 @@ def proj_extras(stream, n: int = 20):
         F.linear(x, w)
 
     def timed(fn):
-        for _ in range(3):
+        for _ in range(10):  # about 8 ms of warm-up: the clocks of an idle GPU take that long to come up
             fn()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -246,8 +246,9 @@ def proj_extras(stream, n: int = 20):
         torch.cuda.synchronize()
         return round(e0.elapsed_time(e1) / n * 1e3, 1)
 
-    res = {"shape": [T, H, W], "fused_us": timed(fused), "gemm_then_region_us": timed(unfused),
-           "gemm_alone_us": timed(gemm)}
+    timed(gemm)  # warm-up of the whole set first
+    res = {"shape": [T, H, W], "gemm_alone_us": timed(gemm), "gemm_then_region_us": timed(unfused),
+           "fused_us": timed(fused)}
     flops = 2 * T * H * W
     res["fused_TFLOPs"] = round(flops / (res["fused_us"] * 1e-6) / 1e12, 1)
     res["fused_frac_of_bf16_mfma_peak"] = round(flops / (res["fused_us"] * 1e-6) / 2.5e15, 3)

@@ -261,6 +261,13 @@ __global__ __launch_bounds__(kProjThreads, 1) void proj_qkv_kernel(const ProjArg
       wkv[8 + c] = proj_bf16_f32(ep_w[1][D / 2 + 8 * k + c]);
     }
     const float inv_d = 1.0f / D;
+    bool any_qk = false;  // a tile of v heads only needs no angles
+#pragma unroll
+    for (int hd = 0; hd < HEADS; ++hd) {
+      int ty, ix;
+      proj_head(a, min(n0 / D + hd, a.heads - 1), ty, ix);
+      any_qk |= ty != 2;
+    }
   #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
   #pragma unroll
@@ -276,11 +283,11 @@ __global__ __launch_bounds__(kProjThreads, 1) void proj_qkv_kernel(const ProjArg
           }
       }
       __syncthreads();
-  #pragma unroll 1
-      for (int lr = threadIdx.x / G; lr < 128; lr += TOK_PER_PASS) {
+  #pragma unroll
+      for (int lr = threadIdx.x / G; lr < 128; lr += TOK_PER_PASS) {  // all passes at once: independent chains
         const int64_t t = m0 + 128 * (lr / 64) + 64 * hf + lr % 64;
         float cs[8], sn[8];
-        if constexpr (ROPE) {
+        if (ROPE && any_qk) {
           const int32_t p = ep_pos[128 * (lr / 64) + 64 * hf + lr % 64];
   #pragma unroll
           for (int c = 0; c < 8; ++c) rope_cos_sin(p, ep_turns[8 * k + c], cs[c], sn[c]);
