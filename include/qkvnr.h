@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define QKVNR_VERSION 10100 /* major * 10000 + minor * 100 + patch */
+#define QKVNR_VERSION 10200 /* major * 10000 + minor * 100 + patch */
 
 /* Return codes. */
 #define QKVNR_OK 0
