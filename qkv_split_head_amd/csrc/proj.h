@@ -13,11 +13,12 @@
 // The product is a plain NT GEMM: x [T, hidden] and w_qkv [width, hidden] are
 // both read along hidden.  Workgroup tile: 256 tokens x 256 packed columns (2
 // heads of 128 or 4 of 64, so every head of the tile is whole), hidden in steps
-// of 64, two LDS stages of 2 x 32 KB filled from registers one step ahead.  Four
-// waves of 128 x 128; the products are taken transposed, C^T = w x^T
+// of 32.  Four LDS stages of 2 x 16 KB are filled by direct-to-LDS loads three
+// steps ahead, so a load has three steps to return before its stage is read.
+// Four waves of 128 x 128; the products are taken transposed, C^T = w x^T
 // (v_mfma_f32_32x32x16_bf16 with the weight rows as the first operand), and the
-// LDS reads, LDS stores and global loads of a step are spread one by one between
-// its MFMAs.  Workgroups are persistent (one per CU) and take the tiles in a
+// fragment reads and global loads of a step are spread one by one between its
+// MFMAs.  Workgroups are persistent (one per CU) and take the tiles in a
 // grouped order that keeps the tiles one XCD runs at once on shared rows.
 // The epilogue moves each half of the tile to LDS as fp32 and finishes it the
 // way the region's forward does: D / 16 threads per token head, a lane-group sum
@@ -32,7 +33,8 @@ namespace qkvnr {
 typedef __bf16 pbf16x8_t __attribute__((ext_vector_type(8)));
 typedef float pf32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kProjBM = 256, kProjBN = 256, kProjBK = 64;
+constexpr int kProjBM = 256, kProjBN = 256, kProjBK = 32;
+constexpr int kProjStages = 4;  // LDS stages of one K step each: three in flight while one is read
 constexpr int kProjThreads = 256;
 constexpr int kProjGroupM = 4;  // token tiles per group of the tile order
 static_assert(kProjThreads == kProjBM, "one thread per token of a tile fills the position table");
@@ -86,12 +88,14 @@ __device__ __forceinline__ void proj_head(const ProjArgs& a, int h, int& type, i
   }
 }
 
-template <int D, bool ROPE>
+template <int D, bool ROPE, bool TAIL>
 __global__ __launch_bounds__(kProjThreads, 1) void proj_qkv_kernel(const ProjArgs a) {
-  constexpr int PIECES = kProjBK / 8;       // 16-byte pieces of a row per K step
-  constexpr int ROWS = kProjBM * PIECES;    // pieces of one operand tile
-  constexpr int PER = kProjBM / (kProjThreads / PIECES);  // rows each thread loads per operand (8)
-  __shared__ uint4 lds[2][2][ROWS];         // [stage][x, w][row * 8 + swizzled piece]: 128 KB
+  constexpr int PIECES = kProjBK / 8;       // 16-byte pieces of a row per K step (4)
+  constexpr int ROWS = kProjBM * PIECES;    // pieces of one operand tile (1024, 16 KB)
+  // four stages of [x, w][row * 4 + swizzled piece], 32 KB each, as four arrays: with the stage of every
+  // access known at compile time the compiler sees that reading one stage does not touch the others
+  // while their direct-to-LDS loads are in flight
+  __shared__ uint4 lds0[2][ROWS], lds1[2][ROWS], lds2[2][ROWS], lds3[2][ROWS];
   __shared__ uint16_t ep_w[2][D];           // q and k norm weights, for the epilogue
   __shared__ double ep_turns[D / 2];        // turns per position of each rotate-half pair
   __shared__ int32_t ep_pos[kProjBM];       // positions of the current tile's tokens
@@ -118,47 +122,54 @@ __global__ __launch_bounds__(kProjThreads, 1) void proj_qkv_kernel(const ProjArg
     n0 = (within / gm) * kProjBN;
   };
 
-  // ---- operand loads: thread t loads piece t mod 8 of rows t / 8 + 32 j (rows past the end clamped)
-  const int q = threadIdx.x % PIECES;
-  int slot[PER];
+  // ---- operand loads, straight from global memory into an LDS stage (global_load_lds_dwordx4: lane
+  // i of an instruction writes the 16 bytes at the instruction's LDS base + 16 i).  Per K step each
+  // wave issues 8 of them: j < 4 for x, j >= 4 for the weight, instruction j covering the 16 rows
+  // 16 (4 w + j % 4) + [0, 16) of its operand.  Lane i fills unit u = 64 (4 w + j % 4) + i of the
+  // stage, row u / 4 position u % 4, so it loads the piece (u % 4) ^ swz(row) of that row
+  // (rows past the end clamped): piece q of row r sits at position q ^ ((r / 4) mod 4), which
+  // puts the 16 rows one fragment read serves on 16 different bank groups.
+  const uint16_t* dsrc[8];
+  auto dma_rows = [&](int64_t gm0, int gn0) {  // the sources' row starts for a tile (column 0, piece offset)
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int r = threadIdx.x / PIECES + (kProjThreads / PIECES) * j;
-    slot[j] = r * PIECES + (q ^ ((r >> 1) & 7));  // the 16 rows one operand read serves hit every bank once
-  }
-  uint4 sa[PER], sb[PER];
-  auto gload = [&](int64_t gm0, int gn0, int kt) {
-    const int off = kt * kProjBK + 8 * q;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int r = threadIdx.x / PIECES + (kProjThreads / PIECES) * j;
-      sa[j] = ld16(a.x + min<int64_t>(gm0 + r, a.T - 1) * a.hidden + off);
-      sb[j] = ld16(a.w + static_cast<int64_t>(min(gn0 + r, a.width - 1)) * a.hidden + off);
+    for (int j = 0; j < 8; ++j) {
+      const int r = 16 * (4 * w + j % 4) + lane / 4;
+      const int off = 8 * ((lane % 4) ^ ((r >> 2) & 3));
+      dsrc[j] = j < 4 ? a.x + min<int64_t>(gm0 + r, a.T - 1) * a.hidden + off
+                      : a.w + static_cast<int64_t>(min(gn0 + r, a.width - 1)) * a.hidden + off;
     }
   };
-  auto lstore = [&](int stage) {
+  auto dma = [&](uint4 (&stg)[2][ROWS], int kt) {  // K step kt of the current tile into a stage
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      lds[stage][0][slot[j]] = sa[j];
-      lds[stage][1][slot[j]] = sb[j];
-    }
+    for (int j = 0; j < 8; ++j)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(dsrc[j] + kt * kProjBK),
+                                       (__attribute__((address_space(3))) void*)(&stg[j / 4][64 * (4 * w + j % 4)]),
+                                       16, 0, 0);
   };
-  auto lds_barrier = [] {  // orders LDS only: the next step's loads stay in flight across it
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-  };
+  // the loads of one K step: 8 per wave; waiting until at most 16 are outstanding leaves the two
+  // later steps in flight and means this wave's loads of the step before them have landed
+  auto wait_step = [] { __builtin_amdgcn_s_waitcnt((1 << 14) | (7 << 4) | (15 << 8)); };  // vmcnt <= 16
 
   // ---- MFMA fragments: step s of a K step, lane l reads piece 2 s + l / 32 of row l mod 32 of a 32-row group
-  const int rr = lane % 32, h = lane / 32, sw = (rr >> 1) & 7;
+  const int rr = lane % 32, h = lane / 32, sw = (rr >> 2) & 3;
   pf32x16_t acc[4][4];  // [packed 32-column tile j][token tile i]
   uint4 fa[2][4], fb[2][4];
-  auto reads = [&](int stage, int s, uint4 (&xa)[4], uint4 (&xb)[4]) {
+  // Each lane's fragment offsets are computed once and hidden from the optimiser, so every read of
+  // a stage forms its address the same way: the waitcnt pass then still sees which stage a read
+  // comes from (an address merged from two different forms costs a wait for every load in flight)
+  int ia[2], ib[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
     const int pos = (2 * s + h) ^ sw;
+    ia[s] = (128 * wm + rr) * PIECES + pos;
+    ib[s] = (128 * wn + rr) * PIECES + pos;
+    asm volatile("" : "+v"(ia[s]), "+v"(ib[s]));
+  }
+  auto reads = [&](const uint4 (&stg)[2][ROWS], int s, uint4 (&xa)[4], uint4 (&xb)[4]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xa[i] = lds[stage][0][(128 * wm + 32 * i + rr) * PIECES + pos];
+    for (int i = 0; i < 4; ++i) xa[i] = stg[0][ia[s] + 32 * i * PIECES];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) xb[j] = lds[stage][1][(128 * wn + 32 * j + rr) * PIECES + pos];
+    for (int j = 0; j < 4; ++j) xb[j] = stg[1][ib[s] + 32 * j * PIECES];
   };
   auto mfmas = [&](const uint4 (&xa)[4], const uint4 (&xb)[4]) {
 #pragma unroll
@@ -169,11 +180,9 @@ __global__ __launch_bounds__(kProjThreads, 1) void proj_qkv_kernel(const ProjArg
                                                             __builtin_bit_cast(pbf16x8_t, xa[i]), acc[j][i], 0, 0, 0);
   };
   // Instruction order inside a K step, one MFMA at a time with the other work between them (the
-  // scheduler is told the pattern, so no burst of reads or stores stalls the matrix unit):
-  //   steps 0-2: 16 MFMAs, the 8 fragment reads of the next step between the first 8
-  //   step 3: 16 MFMAs, with the 16 LDS stores of the next K step and the 16 global loads of the
-  //           K step after next (each load after the store that frees its registers) between
-  //           them; then the barrier and the reads of the next K step's step 0
+  // scheduler is told the pattern, so no burst of reads or loads stalls the matrix unit): step 0's
+  // 16 MFMAs have the 8 fragment reads of step 1 and the 8 loads of the step three ahead between
+  // them; then step 1's 16 MFMAs, the wait for the next step's loads and the barrier.
   auto interleave = [](int reads, int writes, int vloads) {
 #pragma unroll
     for (int m = 0; m < 16; ++m) {
@@ -190,56 +199,49 @@ __global__ __launch_bounds__(kProjThreads, 1) void proj_qkv_kernel(const ProjArg
   const int k = threadIdx.x % G;
   const int KT = a.hidden / kProjBK;
   int L = slot_in_round;
-  int64_t m0 = 0, nm0 = 0;
-  int n0 = 0, nn0 = 0;
-  if (L < tiles) {
-    tile_of(L, m0, n0);
-    gload(m0, n0, 0);  // the first tile's first K step
-  }
+  int64_t m0 = 0;
+  int n0 = 0;
   __syncthreads();     // the epilogue tables above are complete
+  // one K step: the loads of step kt + 3 go to the stage read three steps ago (free since the last
+  // barrier); past the tile's end they reload its last step, unused.  Products only for steps of the tile.
+  auto step = [&](const uint4 (&cur)[2][ROWS], uint4 (&ahead)[2][ROWS], const uint4 (&next)[2][ROWS], int kt) {
+    __builtin_amdgcn_sched_barrier(0);
+    reads(cur, 1, fa[1], fb[1]);
+    dma(ahead, min(kt + 3, KT - 1));
+    if (!TAIL || kt < KT) {  // TAIL: the step count is not a multiple of the stage count
+      mfmas(fa[0], fb[0]);
+      interleave(8, 0, 8);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(fa[1], fb[1]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    wait_step();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    reads(next, 0, fa[0], fb[0]);
+  };
   for (; L < tiles; L += P) {
-    const int Ln = L + P;  // the next tile of this workgroup, whose first K step loads during this one's last
-    if (Ln < tiles) tile_of(Ln, nm0, nn0);
+    tile_of(L, m0, n0);
     if (ROPE) ep_pos[threadIdx.x] = a.pos[min<int64_t>(m0 + threadIdx.x, a.T - 1)];  // kProjThreads == kProjBM
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[j][i] = pf32x16_t{};
-    lstore(0);
-    gload(m0, n0, min(1, KT - 1));
-    lds_barrier();
-    reads(0, 0, fa[0], fb[0]);
-    for (int kt = 0; kt < KT; ++kt) {
-      const int stage = kt & 1;
-      __builtin_amdgcn_sched_barrier(0);
-      reads(stage, 1, fa[1], fb[1]);
-      mfmas(fa[0], fb[0]);
-      interleave(8, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      reads(stage, 2, fa[0], fb[0]);
-      mfmas(fa[1], fb[1]);
-      interleave(8, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      reads(stage, 3, fa[1], fb[1]);
-      mfmas(fa[0], fb[0]);
-      interleave(8, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      // step kt + 1 goes to the other stage (last read before the previous barrier), then the loads
-      // of step kt + 2, or in the last two steps those of the next tile's first step (which waits in
-      // the registers through this tile's epilogue; without a next tile, the last step again).  The
-      // same work on every step keeps the loop free of branches; what the last step stores is unused.
-      const bool here = kt + 2 < KT, next = Ln < tiles;
-      const int64_t gm = here || !next ? m0 : nm0;
-      const int gn = here || !next ? n0 : nn0;
-      const int gk = here ? kt + 2 : (next ? 0 : KT - 1);
-      lstore(stage ^ 1);
-      gload(gm, gn, gk);
-      mfmas(fa[1], fb[1]);
-      interleave(0, 16, 16);
-      __builtin_amdgcn_sched_barrier(0);
-      lds_barrier();
-      reads(stage ^ 1, 0, fa[0], fb[0]);  // past the last step: unused
+    dma_rows(m0, n0);
+    dma(lds0, 0);
+    dma(lds1, min(1, KT - 1));
+    dma(lds2, min(2, KT - 1));
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): nothing of the prologue is left in flight
+    __syncthreads();   // steps 0-2 have landed for every wave (and the position table is written)
+    reads(lds0, 0, fa[0], fb[0]);
+    for (int kt = 0; kt < KT; kt += kProjStages) {
+      step(lds0, lds3, lds1, kt);
+      step(lds1, lds0, lds2, kt + 1);
+      step(lds2, lds1, lds3, kt + 2);
+      step(lds3, lds2, lds0, kt + 3);
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the last loads have landed before LDS is reused
+    __syncthreads();
 
     // ---- epilogue, one half of the tile's tokens at a time (the operand stages are free after the
     // last barrier).  Lane (rr, h) of wave (wm, wn) holds, for token 128 wm + 32 i + rr and packed tile
@@ -250,7 +252,11 @@ __global__ __launch_bounds__(kProjThreads, 1) void proj_qkv_kernel(const ProjArg
     // [8 k, 8 k + 8) of a head and their rotate-half partners [D/2 + 8 k, D/2 + 8 k + 8): the sum of
     // squares is a reduction over the G lanes, and cos / sin of the thread's 8 pairs serve every head
     // of the token.
-    float* ep = reinterpret_cast<float*>(&lds[0][0][0]);  // [128][256] fp32, swizzled granules
+    // [128][256] fp32, swizzled granules: rows 32 s + [0, 32) in stage array s
+    auto eprow = [&](int lr) {
+      uint4* base = lr < 64 ? (lr < 32 ? &lds0[0][0] : &lds1[0][0]) : (lr < 96 ? &lds2[0][0] : &lds3[0][0]);
+      return reinterpret_cast<float*>(base) + (lr & 31) * kProjBN;
+    };
     // the q and k weights of the thread's 16 columns, as fp32 (the same for every token)
     float wqv[16], wkv[16];
   #pragma unroll
@@ -278,7 +284,7 @@ __global__ __launch_bounds__(kProjThreads, 1) void proj_qkv_kernel(const ProjArg
   #pragma unroll
           for (int c = 0; c < 4; ++c) {
             const int g = 32 * wn + 8 * j + 2 * c + h;
-            *reinterpret_cast<float4*>(ep + lr * kProjBN + 4 * (g ^ (lr & 15))) =
+            *reinterpret_cast<float4*>(eprow(lr) + 4 * (g ^ (lr & 15))) =
                 make_float4(acc[j][i][4 * c], acc[j][i][4 * c + 1], acc[j][i][4 * c + 2], acc[j][i][4 * c + 3]);
           }
       }
@@ -292,7 +298,7 @@ __global__ __launch_bounds__(kProjThreads, 1) void proj_qkv_kernel(const ProjArg
   #pragma unroll
           for (int c = 0; c < 8; ++c) rope_cos_sin(p, ep_turns[8 * k + c], cs[c], sn[c]);
         }
-        const float* rowp = ep + lr * kProjBN;
+        const float* rowp = eprow(lr);
   #pragma unroll
         for (int hd = 0; hd < HEADS; ++hd) {
           const int hb = (n0 + hd * D) / D;
@@ -340,8 +346,6 @@ __global__ __launch_bounds__(kProjThreads, 1) void proj_qkv_kernel(const ProjArg
       }
       __syncthreads();
     }
-    m0 = nm0;
-    n0 = nn0;
   }
 }
 

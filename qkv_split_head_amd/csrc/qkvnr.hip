@@ -344,6 +344,12 @@ int gqa_forward(const qkvnr_layout* L, const void* qkv, const int32_t* positions
   return launched("forward");
 }
 
+template <int D, bool ROPE>
+void launch_proj(const ProjArgs& a, bool tail, dim3 grid, dim3 block, hipStream_t stream) {
+  if (tail) hipLaunchKernelGGL((proj_qkv_kernel<D, ROPE, true>), grid, block, 0, stream, a);
+  else hipLaunchKernelGGL((proj_qkv_kernel<D, ROPE, false>), grid, block, 0, stream, a);
+}
+
 }  // namespace
 
 extern "C" {
@@ -632,12 +638,15 @@ int qkvnr_proj_forward(const qkvnr_layout* layout, int64_t hidden, const void* x
   if (rope) fill_turns(a.turns, theta, L->rope_dim);
   // persistent workgroups, one per CU (each holds 130 KB of LDS), or one per tile when there are fewer
   const dim3 grid(static_cast<uint32_t>(std::min<int64_t>(tiles_m * tiles_n, cus))), block(kProjThreads);
+  // the K loop runs in groups of kProjStages steps; a step count that is not a multiple of it takes
+  // the variant that skips the products of the steps past the end
+  const bool tail = (hidden / kProjBK) % kProjStages != 0;
   if (D == 128) {
-    if (rope) hipLaunchKernelGGL((proj_qkv_kernel<128, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((proj_qkv_kernel<128, false>), grid, block, 0, stream, a);
+    if (rope) launch_proj<128, true>(a, tail, grid, block, stream);
+    else launch_proj<128, false>(a, tail, grid, block, stream);
   } else {
-    if (rope) hipLaunchKernelGGL((proj_qkv_kernel<64, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((proj_qkv_kernel<64, false>), grid, block, 0, stream, a);
+    if (rope) launch_proj<64, true>(a, tail, grid, block, stream);
+    else launch_proj<64, false>(a, tail, grid, block, stream);
   }
   return launched("fused projection");
 }
