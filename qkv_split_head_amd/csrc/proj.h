@@ -14,8 +14,9 @@
 // both read along hidden.  Workgroup tile: 256 tokens x 256 packed columns (2
 // heads of 128 or 4 of 64, so every head of the tile is whole), hidden in steps
 // of 32.  Four LDS stages of 2 x 16 KB are filled by direct-to-LDS loads three
-// steps ahead, so a load has three steps to return before its stage is read.
-// Four waves of 128 x 128; the products are taken transposed, C^T = w x^T
+// steps ahead; a load has two steps to return, because the next stage's first
+// fragments are read before the barrier that ends a step.  Four waves of
+// 128 x 128; the products are taken transposed, C^T = w x^T
 // (v_mfma_f32_32x32x16_bf16 with the weight rows as the first operand), and the
 // fragment reads and global loads of a step are spread one by one between its
 // MFMAs.  Workgroups are persistent (one per CU) and take the tiles in a
@@ -146,14 +147,11 @@ __global__ __launch_bounds__(kProjThreads, 1) void proj_qkv_kernel(const ProjArg
                                        (__attribute__((address_space(3))) void*)(&stg[j / 4][64 * (4 * w + j % 4)]),
                                        16, 0, 0);
   };
-  // the loads of one K step: 8 per wave; waiting until at most 16 are outstanding leaves the two
-  // later steps in flight and means this wave's loads of the step before them have landed
-  auto wait_step = [] { __builtin_amdgcn_s_waitcnt((1 << 14) | (7 << 4) | (15 << 8)); };  // vmcnt <= 16
 
   // ---- MFMA fragments: step s of a K step, lane l reads piece 2 s + l / 32 of row l mod 32 of a 32-row group
   const int rr = lane % 32, h = lane / 32, sw = (rr >> 2) & 3;
   pf32x16_t acc[4][4];  // [packed 32-column tile j][token tile i]
-  uint4 fa[2][4], fb[2][4];
+  uint4 fa[3][4], fb[3][4];  // [0] and [2]: first halves of alternate steps; [1]: second halves
   // Each lane's fragment offsets are computed once and hidden from the optimiser, so every read of
   // a stage forms its address the same way: the waitcnt pass then still sees which stage a read
   // comes from (an address merged from two different forms costs a wait for every load in flight)
@@ -180,9 +178,9 @@ __global__ __launch_bounds__(kProjThreads, 1) void proj_qkv_kernel(const ProjArg
                                                             __builtin_bit_cast(pbf16x8_t, xa[i]), acc[j][i], 0, 0, 0);
   };
   // Instruction order inside a K step, one MFMA at a time with the other work between them (the
-  // scheduler is told the pattern, so no burst of reads or loads stalls the matrix unit): step 0's
-  // 16 MFMAs have the 8 fragment reads of step 1 and the 8 loads of the step three ahead between
-  // them; then step 1's 16 MFMAs, the wait for the next step's loads and the barrier.
+  // scheduler is told the pattern, so no burst of reads or loads stalls the matrix unit): the first
+  // half's 16 MFMAs have the second half's 8 fragment reads and the 8 loads of the step three ahead
+  // between them; the second half's 16 MFMAs have the next stage's first 8 fragment reads.
   auto interleave = [](int reads, int writes, int vloads) {
 #pragma unroll
     for (int m = 0; m < 16; ++m) {
@@ -202,23 +200,28 @@ __global__ __launch_bounds__(kProjThreads, 1) void proj_qkv_kernel(const ProjArg
   int64_t m0 = 0;
   int n0 = 0;
   __syncthreads();     // the epilogue tables above are complete
-  // one K step: the loads of step kt + 3 go to the stage read three steps ago (free since the last
-  // barrier); past the tile's end they reload its last step, unused.  Products only for steps of the tile.
-  auto step = [&](const uint4 (&cur)[2][ROWS], uint4 (&ahead)[2][ROWS], const uint4 (&next)[2][ROWS], int kt) {
+  // One K step.  Its fragments of the first half were read during the step before; the second half
+  // is read between the first half's MFMAs, together with the loads of step kt + 3 into the stage
+  // read in the step before (free since the last barrier; past the tile's end they reload its last
+  // step, unused).  The first half of the next stage is read between the second half's MFMAs, so
+  // no read waits on the barrier.  That needs the next stage to be complete one barrier early: the
+  // wait before each barrier leaves only this step's 8 loads per wave in flight, so stage kt + 2
+  // has landed for every wave and a load has two steps to return.  Products only for steps of
+  // the tile.
+  auto step = [&](const uint4 (&cur)[2][ROWS], uint4 (&ahead)[2][ROWS], const uint4 (&next)[2][ROWS], int kt,
+                  uint4 (&a0)[4], uint4 (&b0)[4], uint4 (&a2)[4], uint4 (&b2)[4]) {
     __builtin_amdgcn_sched_barrier(0);
     reads(cur, 1, fa[1], fb[1]);
     dma(ahead, min(kt + 3, KT - 1));
-    if (!TAIL || kt < KT) {  // TAIL: the step count is not a multiple of the stage count
-      mfmas(fa[0], fb[0]);
-      interleave(8, 0, 8);
-      __builtin_amdgcn_sched_barrier(0);
-      mfmas(fa[1], fb[1]);
-    }
+    if (!TAIL || kt < KT) mfmas(a0, b0);
+    interleave(8, 0, 8);
     __builtin_amdgcn_sched_barrier(0);
-    wait_step();
+    reads(next, 0, a2, b2);
+    if (!TAIL || kt < KT) mfmas(fa[1], fb[1]);
+    interleave(8, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8) | 8);  // vmcnt <= 8: only this step's loads in flight
     __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    reads(next, 0, fa[0], fb[0]);
   };
   for (; L < tiles; L += P) {
     tile_of(L, m0, n0);
@@ -231,14 +234,14 @@ __global__ __launch_bounds__(kProjThreads, 1) void proj_qkv_kernel(const ProjArg
     dma(lds0, 0);
     dma(lds1, min(1, KT - 1));
     dma(lds2, min(2, KT - 1));
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): nothing of the prologue is left in flight
-    __syncthreads();   // steps 0-2 have landed for every wave (and the position table is written)
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8) | 8);  // vmcnt <= 8: steps 0 and 1 have landed
+    __syncthreads();   // for every wave (and the position table is written)
     reads(lds0, 0, fa[0], fb[0]);
     for (int kt = 0; kt < KT; kt += kProjStages) {
-      step(lds0, lds3, lds1, kt);
-      step(lds1, lds0, lds2, kt + 1);
-      step(lds2, lds1, lds3, kt + 2);
-      step(lds3, lds2, lds0, kt + 3);
+      step(lds0, lds3, lds1, kt, fa[0], fb[0], fa[2], fb[2]);
+      step(lds1, lds0, lds2, kt + 1, fa[2], fb[2], fa[0], fb[0]);
+      step(lds2, lds1, lds3, kt + 2, fa[0], fb[0], fa[2], fb[2]);
+      step(lds3, lds2, lds0, kt + 3, fa[2], fb[2], fa[0], fb[0]);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the last loads have landed before LDS is reused
     __syncthreads();
