@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define QKVNR_VERSION 10200 /* major * 10000 + minor * 100 + patch */
+#define QKVNR_VERSION 10201 /* major * 10000 + minor * 100 + patch */
 
 /* Return codes. */
 #define QKVNR_OK 0
@@ -149,7 +149,7 @@ int qkvnr_forward(const qkvnr_layout* layout, const void* qkv, const int32_t* po
  *              a bit-exact copy of dv.
  *   dq_norm_w  out [head_dim] fp32, dk_norm_w out [head_dim] fp32: overwritten
  *              with the sums over all tokens and heads.  Block partial sums are
- *              combined with fp32 atomics into 64 workspace slots, so the last
+ *              combined with fp32 atomics into 16 workspace slots, so the last
  *              bits may differ from run to run; a second, one-block launch on
  *              `stream` folds the slots into the outputs.
  *   workspace  device scratch of at least qkvnr_backward_workspace_bytes(layout)
@@ -171,7 +171,7 @@ int qkvnr_backward(const qkvnr_layout* layout, const void* qkv, const int32_t* p
 /* Bytes of workspace qkvnr_backward needs for `layout` (at most
  * QKVNR_BACKWARD_WORKSPACE_MAX for any supported layout). */
 int64_t qkvnr_backward_workspace_bytes(const qkvnr_layout* layout);
-#define QKVNR_BACKWARD_WORKSPACE_MAX 65536
+#define QKVNR_BACKWARD_WORKSPACE_MAX 16384
 
 /*
  * Forward that stores k and v (GQA kinds) or the latent row (LATENT) straight

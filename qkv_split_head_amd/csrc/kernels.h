@@ -59,7 +59,7 @@ constexpr int kBwdDepth = QKVNR_BWD_DEPTH;  // backward iterations whose loads a
 static_assert(kFwdDepth >= 1 && kFwdDepth <= kFwdU, "forward load depth must be in [1, units]");
 static_assert(kBwdDepth >= 1 && kBwdDepth <= kBwdU, "backward load depth must be in [1, units]");
 constexpr int kMaxPairs = 64;           // rotate-half pairs of the widest rotated head (D = 128)
-constexpr int kWgradSlots = 64;         // backward weight-grad partial-sum slots
+constexpr int kWgradSlots = 16;         // backward weight-grad partial-sum slots
 
 enum : int { kInterleaved = 0, kSectioned = 1 };
 
@@ -261,9 +261,11 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_gqa_kernel(const GqaArgs a)
 // ------------------------------------------------------------------ backward
 
 // Weight grads: per lane over the unit, then the wave (shuffles), then the
-// block (LDS), then one fp32 atomic per value into slot (block mod 64) of the
-// workspace (64 slots cut the contention of one shared sum 64-fold);
-// wgrad_fold_kernel then sums the slots.  A single-launch hand-over (the last
+// block (LDS), then one fp32 atomic per value into slot (block mod 16) of the
+// workspace; wgrad_fold_kernel then sums the slots.  Atomics on one address
+// serialise (tens of ns each), so the slot count trades that contention
+// against the fold's reads: with 16 slots a slot's address takes a fifth of
+// the kernel's time in atomics, with 4 most of it.  A single-launch hand-over (the last
 // block to finish folds) would need every block to wait for returning atomics
 // or to fence, which costs more than the second launch on a multi-XCD part.
 // One iteration's backward loads for the lane's head block h: its output
@@ -424,6 +426,7 @@ __global__ __launch_bounds__(kFoldThreads) void wgrad_fold_kernel(float* slots, 
   constexpr int n = 2 * D;
   constexpr int Q = kFoldThreads / n;  // 4 for D = 128, 8 for D = 64
   constexpr int PER = kWgradSlots / Q;
+  static_assert(kWgradSlots % Q == 0, "every thread of the fold sums the same number of slots");
   __shared__ float part[kFoldThreads];
   const int i = threadIdx.x % n, q = threadIdx.x / n;
   float v[PER];
