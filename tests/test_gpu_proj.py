@@ -77,6 +77,7 @@ CASES = [
     ("interleaved", 2000, 256, 16, 8, 64, True, "random"),
     ("sectioned", 700, 64, 8, 4, 128, False, "arange"),     # two K steps per tile, several tiles per workgroup
     ("sectioned", 333, 96, 2, 2, 128, True, "random"),      # three K steps: fewer than the stage count
+    ("interleaved", 40, 32, 1, 2, 64, True, "random"),      # one K step
 ]
 
 
