@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define QKVNR_VERSION 10201 /* major * 10000 + minor * 100 + patch */
+#define QKVNR_VERSION 10300 /* major * 10000 + minor * 100 + patch */
 
 /* Return codes. */
 #define QKVNR_OK 0
@@ -274,7 +274,8 @@ int qkvnr_gram_partials(int64_t blocks, int32_t d, int64_t cols, const void* x, 
  * (||G||_F + eps)^2 (the norm is the square root of its trace) and P by
  * (||G||_F + eps), so that P G is the first step from G / (||G||_F + eps).  P is
  * multiplied by `scale` (pass the block scale max(1, rows/cols)**0.5 on the
- * last step, 1 otherwise).  The update P X is the caller's batched GEMM.
+ * last step, 1 otherwise).  The update P X is qkvnr_ns_update (or any batched
+ * GEMM).
  *
  *   dtype   QKVNR_BF16 or QKVNR_FP32: the type of p.
  *   blocks  number of blocks, >= 0 (0 is a no-op).
@@ -286,6 +287,29 @@ int qkvnr_gram_partials(int64_t blocks, int32_t d, int64_t cols, const void* x, 
  */
 int qkvnr_ns_poly(int32_t dtype, int64_t blocks, int32_t d, float* gram, int32_t parts,
                   int32_t first, float scale, float eps, void* p, hipStream_t stream);
+
+/*
+ * One Newton-Schulz update of bf16 blocks, Y = P X per block (fp32 products,
+ * rounded once to bf16), and optionally the partial Gram matrices Y Y^T that
+ * the next step's qkvnr_ns_poly needs, taken from the same pass: Y is written
+ * once and not read back.  (DeepSpeed page, "What this PR does": each head
+ * block is orthogonalised on its own; every step is X <- P X.)
+ *
+ *   blocks  number of blocks, 0 .. 2^31 - 1 (0 is a no-op).
+ *   d       block side: 64 or 128 (others QKVNR_EUNSUPPORTED).
+ *   cols    block width, a positive multiple of 8 (QKVNR_EALIGN otherwise), at
+ *           most 2^30 (QKVNR_EINVAL otherwise).
+ *   p       [blocks, d, d] bf16, row-major, 16-byte aligned (qkvnr_ns_poly's
+ *           bf16 output).
+ *   x       [blocks, d, cols] bf16, row-major, 16-byte aligned.
+ *   y       out [blocks, d, cols] bf16, 16-byte aligned; must not overlap x or p.
+ *   parts   column slices, 1..65535, as for qkvnr_gram_partials.
+ *   gram    NULL, or out [blocks, parts, d, d] fp32, 4-byte aligned, must not
+ *           overlap p, x or y: what qkvnr_gram_partials(blocks, d, cols, y,
+ *           parts, gram) would write, up to the order of the fp32 sums.
+ */
+int qkvnr_ns_update(int64_t blocks, int32_t d, int64_t cols, const void* p, const void* x, void* y,
+                    int32_t parts, float* gram, hipStream_t stream);
 
 /*
  * The QKV projection with the forward region fused into its epilogue.

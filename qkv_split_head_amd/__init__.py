@@ -41,6 +41,7 @@ from ._binding import (  # noqa: F401
     qkvnr_fused_head_blocks,
     qkvnr_gram_partials,
     qkvnr_ns_poly,
+    qkvnr_ns_update,
     qkvnr_proj_forward,
     qkvnr_rope_inplace,
     rope_inplace,

@@ -88,6 +88,9 @@ def lib() -> ctypes.CDLL:
         L.qkvnr_ns_poly.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, vp, ctypes.c_int32,
                                     ctypes.c_int32, ctypes.c_float, ctypes.c_float, vp, vp]
         L.qkvnr_ns_poly.restype = ctypes.c_int
+        L.qkvnr_ns_update.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int64, vp, vp, vp, ctypes.c_int32,
+                                      vp, vp]
+        L.qkvnr_ns_update.restype = ctypes.c_int
         L.qkvnr_proj_forward.argtypes = [lp, ctypes.c_int64, vp, vp, i32p, vp, vp, ctypes.c_float, ctypes.c_double,
                                          vp, vp, vp, vp]
         L.qkvnr_proj_forward.restype = ctypes.c_int
@@ -202,6 +205,11 @@ def qkvnr_ns_poly(dtype: int, blocks: int, d: int, gram, parts: int, first: bool
     """Call ``qkvnr_ns_poly``."""
     _check(lib().qkvnr_ns_poly(dtype, blocks, d, _ptr(gram), parts, 1 if first else 0, scale, eps, _ptr(p),
                                _stream(stream)))
+
+
+def qkvnr_ns_update(blocks: int, d: int, cols: int, p, x, y, parts: int, gram=None, stream=None) -> None:
+    """Call ``qkvnr_ns_update`` (``gram`` None: no Gram partials)."""
+    _check(lib().qkvnr_ns_update(blocks, d, cols, _ptr(p), _ptr(x), _ptr(y), parts, _ptr(gram), _stream(stream)))
 
 
 def qkvnr_proj_forward(layout: Layout, hidden: int, x, w_qkv, positions, q_norm_w, k_norm_w, eps: float,

@@ -256,4 +256,162 @@ __global__ __launch_bounds__(kNsThreads) void ns_poly_kernel(const float* __rest
   }
 }
 
+// One Newton-Schulz update of bf16 blocks, Y = P X, and (GRAM) the partial Gram matrices of Y
+// that the next step needs, from the same pass over X: Y is written once and never read back.
+// p [blocks, D, D] bf16, x and y [blocks, D, cols] bf16 (row stride cols), gout [blocks, parts,
+// D, D] fp32 over the column slices of gram_partials_kernel.  One workgroup per (block, slice),
+// D / 32 waves, chunks of 64 columns:
+// - X's chunk is loaded into registers three chunks ahead, thread (rg, cg) holding rows
+//   4 rg + [0, 4) of columns 8 cg + [0, 8), and written to LDS transposed (X^T, rows of D values
+//   along k): column n's 4 values go to piece k / 8 of row n at position (k / 8) ^ (n mod D/8);
+// - the product is taken as Y^T = X^T P^T: the A operand is a row of X^T and the B operand a row
+//   of P, so P needs no transpose, and each lane keeps its P operands in registers for the whole
+//   slice.  Wave w forms rows 32 w + [0, 32) of Y for the chunk's 64 columns;
+// - Y is rounded to bf16 into LDS in the Gram layout (piece q of row r at q ^ ((r / 2) mod 8);
+//   columns past the slice are zero), then stored with 16-byte writes and, for GRAM, its chunk
+//   products are added as in gram_partials_kernel.
+// Software pipelined, one barrier a chunk: between two barriers a wave forms chunk c's product
+// (from X^T buffer c mod 2), stores and adds the Gram products of chunk c - 1 (Y buffer
+// (c - 1) mod 2), writes chunk c + 1's X^T and then chunk c's Y.  A buffer is rewritten only
+// after the barrier that follows its last reads.  64 KB of LDS: two workgroups fit on a CU.
+template <int D, bool GRAM>
+__global__ __launch_bounds__(kWave * (D / 32), 2) void ns_update_kernel(const uint16_t* __restrict__ p,
+                                                                       const uint16_t* __restrict__ x,
+                                                                       uint16_t* __restrict__ y, int cols, int slice,
+                                                                       float* __restrict__ gout) {
+  static_assert(D == 64 || D == 128, "block sides 64 and 128");
+  constexpr int T = D / 32, THREADS = kWave * T;
+  constexpr int XP = D / 8;                  // 16-byte pieces of an X^T row
+  constexpr int YP = kGramChunk / 8;         // 16-byte pieces of a Y row
+  constexpr int KS = D / 16;                 // MFMA steps over k for the product
+  static_assert(THREADS == 2 * D, "one thread per 4 x 8 patch of a chunk");
+  __shared__ uint4 xt[2][kGramChunk * XP];
+  __shared__ uint4 ys[2][D * YP];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+  const int64_t blk = blockIdx.x;
+  const int part = blockIdx.y, parts = gridDim.y;
+  const int k0 = part * slice, kend = min(cols, k0 + slice);
+  const int chunks = kend > k0 ? (kend - k0 + kGramChunk - 1) / kGramChunk : 0;
+  const int rr = lane % 32, h = lane / 32;
+
+  // P operands of this lane: row 32 w + rr, k = 16 s + 8 h + [0, 8)
+  uint4 pf[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) pf[s] = ld16(p + (blk * D + 32 * w + rr) * D + 16 * s + 8 * h);
+
+  const int rg = threadIdx.x / 8, cg = threadIdx.x % 8;
+  const uint16_t* xr = x + (blk * D + 4 * rg) * static_cast<int64_t>(cols);
+  auto load = [&](int c, uint4 (&v)[4]) {
+    const int col = min(k0 + c * kGramChunk + 8 * cg, cols - 8);  // clamped into the row
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = ld16(xr + static_cast<int64_t>(i) * cols + col);
+  };
+  auto store_xt = [&](const uint4 (&v)[4], uint4* buf) {
+    const int k = 4 * rg;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {  // dword d of a row holds columns 2 d (low half) and 2 d + 1
+      const uint32_t a0 = (&v[0].x)[d], a1 = (&v[1].x)[d], a2 = (&v[2].x)[d], a3 = (&v[3].x)[d];
+      const uint2 lo = make_uint2((a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16));
+      const uint2 hi = make_uint2((a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u));
+      const int n0 = 8 * cg + 2 * d, n1 = n0 + 1;
+      reinterpret_cast<uint2*>(&buf[n0 * XP + ((k >> 3) ^ (n0 & (XP - 1)))])[(k >> 2) & 1] = lo;
+      reinterpret_cast<uint2*>(&buf[n1 * XP + ((k >> 3) ^ (n1 & (XP - 1)))])[(k >> 2) & 1] = hi;
+    }
+  };
+  auto lds_barrier = [] {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  };
+
+  const int sw = (rr >> 1) & 7;  // Gram layout swizzle of rows 32 t + rr
+  f32x16_t acc[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) acc[t] = f32x16_t{};
+
+  auto product = [&](const uint4* xb, f32x16_t (&ya)[2]) {  // Y^T of the chunk's two 32-column tiles
+    ya[0] = ya[1] = f32x16_t{};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) {
+        const int n = 32 * ni + rr;
+        const uint4 af = xb[n * XP + ((2 * s + h) ^ (n & (XP - 1)))];
+        ya[ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af),
+                                                         __builtin_bit_cast(bf16x8_t, pf[s]), ya[ni], 0, 0, 0);
+      }
+  };
+  // lane (rr, h) holds Y[32 w + rr][32 ni + 8 q + 4 h + r] in register 4 q + r of ya[ni]
+  auto write_y = [&](int c, const f32x16_t (&ya)[2], uint4* yb) {
+    const int cbase = k0 + c * kGramChunk, m = 32 * w + rr;
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int piece = 4 * ni + q;
+        const bool in = cbase + 8 * piece < kend;
+        const uint2 val = in ? make_uint2(pack_bf16x2(ya[ni][4 * q], ya[ni][4 * q + 1]),
+                                          pack_bf16x2(ya[ni][4 * q + 2], ya[ni][4 * q + 3]))
+                             : make_uint2(0u, 0u);
+        reinterpret_cast<uint2*>(&yb[m * YP + (piece ^ ((m >> 1) & 7))])[h] = val;
+      }
+  };
+  auto finish = [&](int c, const uint4* yb) {  // chunk c's stores and Gram products, from its Y buffer
+    const int cbase = k0 + c * kGramChunk;
+#pragma unroll
+    for (int j = 0; j < D * YP / THREADS; ++j) {
+      const int u = threadIdx.x + j * THREADS, row = u / YP, q = u % YP;
+      const int col = cbase + 8 * q;
+      if (col < kend) st16(y + (blk * D + row) * static_cast<int64_t>(cols) + col, yb[row * YP + (q ^ ((row >> 1) & 7))]);
+    }
+    if constexpr (GRAM) {
+#pragma unroll
+      for (int st = 0; st < kGramChunk / 16; ++st) {
+        const int pos = (2 * st + h) ^ sw;
+        const uint4 a = yb[(32 * w + rr) * YP + pos];
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const uint4 b = yb[(32 * t + rr) * YP + pos];
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                           __builtin_bit_cast(bf16x8_t, b), acc[t], 0, 0, 0);
+        }
+      }
+    }
+  };
+  // phase c: the loads, LDS writes and barrier run on every path; the products, stores and Gram
+  // products only for chunks of the slice (the same for the whole workgroup)
+  auto phase = [&](int c, uint4 (&vn)[4], int b) {
+    f32x16_t ya[2];
+    if (c < chunks) product(xt[b], ya);
+    if (c >= 1 && c - 1 < chunks) finish(c - 1, ys[b ^ 1]);
+    store_xt(vn, xt[b ^ 1]);  // chunk c + 1
+    load(c + 3, vn);
+    if (c < chunks) write_y(c, ya, ys[b]);
+    lds_barrier();
+  };
+  // chunk c + 1 is in v[(c + 1) mod 2] when phase c starts
+  uint4 v0[4], v1[4];
+  load(0, v0);
+  load(1, v1);
+  store_xt(v0, xt[0]);
+  load(2, v0);
+  lds_barrier();
+  for (int c0 = 0; c0 < chunks; c0 += 2) {
+    phase(c0, v1, 0);
+    phase(c0 + 1, v0, 1);
+  }
+  // the last chunk's stores and Gram products: the loop's phase c = chunks has done them unless
+  // chunks is even, where the loop ends at c = chunks - 1
+  if (chunks > 0 && chunks % 2 == 0) finish(chunks - 1, ys[(chunks - 1) & 1]);
+  if constexpr (GRAM) {
+    float* o = gout + (blk * parts + part) * D * D;
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        o[(32 * w + 8 * (e / 4) + 4 * h + e % 4) * D + 32 * t + rr] = acc[t][e];
+  }
+}
+
 }  // namespace qkvnr

@@ -528,6 +528,9 @@ int qkvnr_gram_partials(int64_t blocks, int32_t d, int64_t cols, const void* x, 
   if (cols > (1 << 30)) return fail(QKVNR_EINVAL, "cols %lld above 2^30", (long long)cols);
   if (parts < 1 || parts > 65535) return fail(QKVNR_EINVAL, "parts %d out of [1, 65535]", parts);
   if (blocks == 0) return QKVNR_OK;
+  if (blocks > (INT64_MAX / 8) / (int64_t(d) * std::max<int64_t>(cols, int64_t(parts) * d)))
+    return fail(QKVNR_EINVAL, "%lld blocks of %d x %lld do not fit a 64-bit byte count", (long long)blocks, d,
+                (long long)cols);
   if (int rc = need16(x, "x")) return rc;
   if (int rc = need4(out, "out")) return rc;
   const int64_t n_out = blocks * parts * d * d;
@@ -576,6 +579,45 @@ int qkvnr_ns_poly(int32_t dtype, int64_t blocks, int32_t d, float* gram, int32_t
     else hipLaunchKernelGGL((ns_poly_kernel<float, 0>), grid, dim3(kNsThreads), 0, stream, gram, o, d, parts, fi, scale, eps);
   }
   return launched("Newton-Schulz polynomial");
+}
+
+int qkvnr_ns_update(int64_t blocks, int32_t d, int64_t cols, const void* p, const void* x, void* y,
+                    int32_t parts, float* gram, hipStream_t stream) {
+  if (blocks < 0 || blocks > INT32_MAX) return fail(QKVNR_EINVAL, "blocks %lld out of [0, 2^31)", (long long)blocks);
+  if (d != 64 && d != 128) return fail(QKVNR_EUNSUPPORTED, "block side %d: the update kernel exists for 64 and 128", d);
+  if (cols < 1 || cols % 8) return fail(QKVNR_EALIGN, "cols %lld must be a positive multiple of 8", (long long)cols);
+  if (cols > (1 << 30)) return fail(QKVNR_EINVAL, "cols %lld above 2^30", (long long)cols);
+  if (parts < 1 || parts > 65535) return fail(QKVNR_EINVAL, "parts %d out of [1, 65535]", parts);
+  if (blocks == 0) return QKVNR_OK;
+  if (blocks > (INT64_MAX / 8) / (int64_t(d) * std::max<int64_t>(cols, int64_t(parts) * d)))
+    return fail(QKVNR_EINVAL, "%lld blocks of %d x %lld do not fit a 64-bit byte count", (long long)blocks, d,
+                (long long)cols);
+  if (int rc = need16(p, "p")) return rc;
+  if (int rc = need16(x, "x")) return rc;
+  if (int rc = need16(y, "y")) return rc;
+  if (gram) {
+    if (int rc = need4(gram, "gram")) return rc;
+  }
+  const int64_t xb = blocks * d * cols * 2, pb = blocks * d * d * 2, gb = blocks * parts * d * d * 4;
+  if (overlaps({y, xb}, {x, xb}) || overlaps({y, xb}, {p, pb})) return fail(QKVNR_EINVAL, "y overlaps x or p");
+  if (gram && (overlaps({gram, gb}, {x, xb}) || overlaps({gram, gb}, {y, xb}) || overlaps({gram, gb}, {p, pb})))
+    return fail(QKVNR_EINVAL, "gram overlaps p, x or y");
+  int cus = 0;
+  if (int rc = current_device(&cus)) return rc;
+  const int sl = static_cast<int>(((cols + parts - 1) / parts + 15) / 16 * 16);  // the Gram kernel's slices
+  const dim3 g(static_cast<uint32_t>(blocks), static_cast<uint32_t>(parts));
+  const auto* ps = static_cast<const uint16_t*>(p);
+  const auto* xs = static_cast<const uint16_t*>(x);
+  auto* ys = static_cast<uint16_t*>(y);
+  const int c = static_cast<int>(cols);
+  if (d == 128) {
+    if (gram) hipLaunchKernelGGL((ns_update_kernel<128, true>), g, dim3(kWave * 4), 0, stream, ps, xs, ys, c, sl, gram);
+    else hipLaunchKernelGGL((ns_update_kernel<128, false>), g, dim3(kWave * 4), 0, stream, ps, xs, ys, c, sl, gram);
+  } else {
+    if (gram) hipLaunchKernelGGL((ns_update_kernel<64, true>), g, dim3(kWave * 2), 0, stream, ps, xs, ys, c, sl, gram);
+    else hipLaunchKernelGGL((ns_update_kernel<64, false>), g, dim3(kWave * 2), 0, stream, ps, xs, ys, c, sl, gram);
+  }
+  return launched("Newton-Schulz update");
 }
 
 int qkvnr_proj_forward(const qkvnr_layout* layout, int64_t hidden, const void* x, const void* w_qkv,

@@ -13,8 +13,11 @@ P = a I + b X X^T + c (X X^T)^2: this library's ``qkvnr_gram_partials`` (the
 Gram matrices with MFMA, reading both factors as rows of X; bf16 blocks of
 side 32..128), ``qkvnr_ns_poly`` (P from the Gram matrices, with the first
 step's Frobenius normalisation and the last step's block scale folded in), and
-the update P X as a plain batched library GEMM.  The blocks never leave the
-``[blocks, d, in]`` layout between steps.
+the update P X.  For bf16 blocks of side 64 or 128 the update is
+``qkvnr_ns_update``, which also forms the next step's Gram matrices from the
+new X in the same pass, so only the first step reads X for its Gram matrices
+alone.  Other blocks take a plain batched library GEMM.  The blocks never leave
+the ``[blocks, d, in]`` layout between steps.
 
 ``compute_dtype`` bf16 is Muon's usual precision (GEMMs in bf16 with fp32
 accumulation); fp32 runs the same steps in fp32.
@@ -50,6 +53,15 @@ def _newton_schulz_blocks(X: torch.Tensor, scale: float, steps: int, eps: float)
     own_gram = X.dtype == torch.bfloat16 and d in (32, 64, 96, 128) and cols % 8 == 0
     parts = _gram_parts(nb, cols) if own_gram else 1
     gram = torch.empty((nb, parts, d, d), dtype=torch.float32, device=X.device)
+    if own_gram and d in (64, 128):  # fused update: Y = P X and Y's Gram matrices in one pass
+        b.qkvnr_gram_partials(nb, d, cols, X, parts, gram)
+        bufs = (torch.empty_like(X), torch.empty_like(X))
+        for i in range(steps):
+            b.qkvnr_ns_poly(dtype, nb, d, gram, parts, i == 0, scale if i == steps - 1 else 1.0, eps, P)
+            Y = bufs[i % 2]
+            b.qkvnr_ns_update(nb, d, cols, P, X, Y, parts, gram if i < steps - 1 else None)
+            X = Y
+        return X
     for i in range(steps):
         if own_gram:   # the library kernel reads both factors as rows of X
             b.qkvnr_gram_partials(nb, d, cols, X, parts, gram)

@@ -292,7 +292,41 @@ def test_gram_partials_argument_checks():
     assert call(i3=A + 8) == qk.EALIGN
     assert call(i5=B + 2) == qk.EALIGN
     assert call(i5=A + 4096) == qk.EINVAL         # out overlaps x
+    assert call(i0=(1 << 31) - 1, i2=1 << 30) == qk.EINVAL   # byte counts past 2^63
     assert call(i0=0, i3=0, i5=0) == qk.OK
+
+
+def test_ns_update_argument_checks():
+    f = qk.lib().qkvnr_ns_update
+    # blocks, d, cols, p, x, y, parts, gram
+    ok = [48, 128, 4096, A, B, C, 11, Dp]
+
+    def call(**change):
+        a = list(ok)
+        for i, v in change.items():
+            a[int(i[1:])] = v
+        return f(*a, None)
+
+    assert call(i0=-1) == qk.EINVAL
+    assert call(i0=1 << 31) == qk.EINVAL
+    assert call(i1=96) == qk.EUNSUPPORTED
+    assert call(i1=32) == qk.EUNSUPPORTED
+    assert call(i2=4100) == qk.EALIGN            # cols not a multiple of 8
+    assert call(i2=0) == qk.EALIGN
+    assert call(i2=(1 << 30) + 8) == qk.EINVAL
+    assert call(i6=0) == qk.EINVAL               # parts
+    assert call(i6=65536) == qk.EINVAL
+    assert call(i0=(1 << 31) - 1, i2=1 << 30) == qk.EINVAL   # byte counts past 2^63
+    assert call(i3=A + 8) == qk.EALIGN           # p
+    assert call(i4=B + 8) == qk.EALIGN           # x
+    assert call(i5=C + 8) == qk.EALIGN           # y
+    assert call(i7=Dp + 2) == qk.EALIGN          # gram
+    assert call(i5=B + 4096) == qk.EINVAL        # y overlaps x
+    assert call(i5=A + 64) == qk.EINVAL          # y overlaps p
+    assert call(i7=B + 4096) == qk.EINVAL        # gram overlaps x
+    assert call(i7=C + 16) == qk.EINVAL          # gram overlaps y
+    assert call(i7=A + 16) == qk.EINVAL          # gram overlaps p
+    assert call(i0=0, i3=0, i4=0, i5=0, i7=0) == qk.OK   # no blocks: nothing is touched
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

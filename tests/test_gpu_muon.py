@@ -96,6 +96,37 @@ def test_gram_partials_match_the_products(blocks, d, cols, parts):
     np.testing.assert_allclose(got.sum(axis=1), full, rtol=1e-5, atol=1e-5 * np.abs(full).max())
 
 
+# ragged chunk tails (1000, 1064, 40 and 24 columns), an empty slice (40 columns in 4 slices of 16),
+# both block sides, with and without the Gram matrices
+@pytest.mark.parametrize("blocks,d,cols,parts", [(3, 128, 1000, 3), (48, 128, 4096, 5), (2, 64, 1064, 2),
+                                                  (1, 128, 40, 4), (5, 64, 24, 1)])
+@pytest.mark.parametrize("with_gram", [True, False])
+def test_ns_update_matches_the_products(blocks, d, cols, parts, with_gram):
+    rng = np.random.default_rng(blocks * d + cols + parts)
+    x = torch.from_numpy(rng.standard_normal((blocks, d, cols)).astype(np.float32)).cuda().to(torch.bfloat16)
+    p = torch.from_numpy((rng.standard_normal((blocks, d, d)) / np.sqrt(d)).astype(np.float32)).cuda()
+    p = p.to(torch.bfloat16)
+    y = torch.full_like(x, float("nan"))
+    gram = torch.full((blocks, parts, d, d), float("nan"), device="cuda") if with_gram else None
+    qk.qkvnr_ns_update(blocks, d, cols, p, x, y, parts, gram)
+    torch.cuda.synchronize()
+    xs = x.float().cpu().numpy().astype(np.float64)
+    ps = p.float().cpu().numpy().astype(np.float64)
+    got = y.float().cpu().numpy().astype(np.float64)
+    want = np.matmul(ps, xs)
+    # one rounding to bf16 (at most 2^-8 relative) of an fp32 sum of d products (within
+    # d 2^-24 sum |p x| of the exact sum)
+    acc_err = d * 2.0 ** -24 * np.matmul(np.abs(ps), np.abs(xs))
+    assert np.all(np.abs(got - want) <= 2.0 ** -8 * np.abs(want) + 2 * acc_err + 1e-30)
+    if with_gram:
+        S = ((cols + parts - 1) // parts + 15) // 16 * 16
+        g = gram.cpu().numpy().astype(np.float64)
+        for q in range(parts):
+            sl = got[:, :, q * S:min(cols, (q + 1) * S)]   # the stored bf16 values of Y
+            w = np.einsum("bik,bjk->bij", sl, sl)
+            np.testing.assert_allclose(g[:, q], w, rtol=1e-5, atol=1e-5 * max(1.0, np.abs(w).max()))
+
+
 def test_declined_weights_raise():
     g = torch.zeros((80, 64), device="cuda")   # the Falcon shape: config total 192 rows, weight 80
     with pytest.raises(qk.QkvnrError):
