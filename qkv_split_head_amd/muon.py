@@ -87,7 +87,10 @@ def per_head_newton_schulz(G: torch.Tensor, n_q: int, n_kv: int, head_dim: int, 
     dt = G.dtype if compute_dtype is None else compute_dtype
     if dt not in (torch.bfloat16, torch.float32):
         raise ValueError(f"unsupported compute dtype {dt}")
-    X = G.to(dt).contiguous().view(nb, head_dim, cols)
+    X = G.to(dt).contiguous()
+    if X.data_ptr() % 16:   # the kernels read 16 bytes at a time: an offset view gets an aligned copy
+        X = X.clone()
+    X = X.view(nb, head_dim, cols)
     scale = max(1.0, head_dim / cols) ** 0.5
     if head_dim <= cols:
         return _newton_schulz_blocks(X, scale, steps, eps).view(rows, cols)

@@ -127,6 +127,19 @@ def test_ns_update_matches_the_products(blocks, d, cols, parts, with_gram):
             np.testing.assert_allclose(g[:, q], w, rtol=1e-5, atol=1e-5 * max(1.0, np.abs(w).max()))
 
 
+def test_weight_at_an_unaligned_offset():
+    # a weight that is a view 2 bytes into a flat buffer: updated like an aligned copy of itself
+    rng = np.random.default_rng(5)
+    rows, cols = (4 + 2 * 2) * 64, 512
+    flat = torch.from_numpy(rng.standard_normal(rows * cols + 1).astype(np.float32)).cuda().to(torch.bfloat16)
+    g = flat[1:].view(rows, cols)
+    assert g.data_ptr() % 16 != 0
+    got = per_head_newton_schulz(g, 4, 2, 64)
+    want = per_head_newton_schulz(g.clone(), 4, 2, 64)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), want.view(torch.int16))
+
+
 def test_declined_weights_raise():
     g = torch.zeros((80, 64), device="cuda")   # the Falcon shape: config total 192 rows, weight 80
     with pytest.raises(qk.QkvnrError):
