@@ -326,7 +326,7 @@ int qkvnr_ns_update(int64_t blocks, int32_t d, int64_t cols, const void* p, cons
  *              QKVNR_EUNSUPPORTED), T, n_kv, q_per_kv, head_dim, rope_dim and
  *              width as for qkvnr_forward; in_row_stride is not used (there is
  *              no packed tensor) but must pass the same check (>= width).
- *   hidden     columns of x and w_qkv: a positive multiple of 32, at most 2^30
+ *   hidden     columns of x and w_qkv: a positive multiple of 64, at most 2^30
  *              (QKVNR_EINVAL otherwise).
  *   x          [T, hidden] bf16, row-major, 16-byte aligned.
  *   w_qkv      [width, hidden] bf16, row-major, 16-byte aligned: row j is packed

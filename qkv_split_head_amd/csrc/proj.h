@@ -13,13 +13,12 @@
 // The product is a plain NT GEMM: x [T, hidden] and w_qkv [width, hidden] are
 // both read along hidden.  Workgroup tile: 256 tokens x 256 packed columns (2
 // heads of 128 or 4 of 64, so every head of the tile is whole), hidden in steps
-// of 32.  Four LDS stages of 2 x 16 KB are filled by direct-to-LDS loads three
-// steps ahead; a load has two steps to return, because the next stage's first
-// fragments are read before the barrier that ends a step.  Four waves of
-// 128 x 128; the products are taken transposed, C^T = w x^T
-// (v_mfma_f32_32x32x16_bf16 with the weight rows as the first operand), and the
-// fragment reads and global loads of a step are spread one by one between its
-// MFMAs.  Workgroups are persistent (one per CU) and take the tiles in a
+// of 64.  Two LDS stages of 2 x 32 KB are filled by direct-to-LDS loads one step
+// ahead: a load has one step (64 MFMAs a wave) to return, and a step ends with
+// one wait and one barrier.  Four waves of 128 x 128; the products are taken
+// transposed, C^T = w x^T (v_mfma_f32_32x32x16_bf16 with the weight rows as the
+// first operand), and the fragment reads and global loads of a step are spread
+// one by one between its MFMAs.  Workgroups are persistent (one per CU) and take the tiles in a
 // grouped order that keeps the tiles one XCD runs at once on shared rows.
 // The epilogue moves each half of the tile to LDS as fp32 and finishes it the
 // way the region's forward does: D / 16 threads per token head, a lane-group sum
@@ -34,8 +33,8 @@ namespace qkvnr {
 typedef __bf16 pbf16x8_t __attribute__((ext_vector_type(8)));
 typedef float pf32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kProjBM = 256, kProjBN = 256, kProjBK = 32;
-constexpr int kProjStages = 4;  // LDS stages of one K step each: three in flight while one is read
+constexpr int kProjBM = 256, kProjBN = 256, kProjBK = 64;
+constexpr int kProjStages = 2;  // LDS stages of one K step each: one loading while the other is read
 constexpr int kProjThreads = 256;
 constexpr int kProjGroupM = 4;  // token tiles per group of the tile order
 static_assert(kProjThreads == kProjBM, "one thread per token of a tile fills the position table");
@@ -91,12 +90,12 @@ __device__ __forceinline__ void proj_head(const ProjArgs& a, int h, int& type, i
 
 template <int D, bool ROPE, bool TAIL>
 __global__ __launch_bounds__(kProjThreads, 1) void proj_qkv_kernel(const ProjArgs a) {
-  constexpr int PIECES = kProjBK / 8;       // 16-byte pieces of a row per K step (4)
-  constexpr int ROWS = kProjBM * PIECES;    // pieces of one operand tile (1024, 16 KB)
+  constexpr int PIECES = kProjBK / 8;       // 16-byte pieces of a row per K step (8)
+  constexpr int ROWS = kProjBM * PIECES;    // pieces of one operand tile (2048, 32 KB)
   // four stages of [x, w][row * 4 + swizzled piece], 32 KB each, as four arrays: with the stage of every
   // access known at compile time the compiler sees that reading one stage does not touch the others
   // while their direct-to-LDS loads are in flight
-  __shared__ uint4 lds0[2][ROWS], lds1[2][ROWS], lds2[2][ROWS], lds3[2][ROWS];
+  __shared__ uint4 lds0[2][ROWS], lds1[2][ROWS];
   __shared__ uint16_t ep_w[2][D];           // q and k norm weights, for the epilogue
   __shared__ double ep_turns[D / 2];        // turns per position of each rotate-half pair
   __shared__ int32_t ep_pos[kProjBM];       // positions of the current tile's tokens
@@ -125,49 +124,44 @@ __global__ __launch_bounds__(kProjThreads, 1) void proj_qkv_kernel(const ProjArg
 
   // ---- operand loads, straight from global memory into an LDS stage (global_load_lds_dwordx4: lane
   // i of an instruction writes the 16 bytes at the instruction's LDS base + 16 i).  Per K step each
-  // wave issues 8 of them: j < 4 for x, j >= 4 for the weight, instruction j covering the 16 rows
-  // 16 (4 w + j % 4) + [0, 16) of its operand.  Lane i fills unit u = 64 (4 w + j % 4) + i of the
-  // stage, row u / 4 position u % 4, so it loads the piece (u % 4) ^ swz(row) of that row
-  // (rows past the end clamped): piece q of row r sits at position q ^ ((r / 4) mod 4), which
-  // puts the 16 rows one fragment read serves on 16 different bank groups.
-  const uint16_t* dsrc[8];
+  // wave issues 16 of them: j < 8 for x, j >= 8 for the weight, instruction j covering the 8 rows
+  // 8 (8 w + j % 8) + [0, 8) of its operand.  Lane i fills unit u = 64 (8 w + j % 8) + i of the
+  // stage, row u / 8 position u % 8, so it loads the piece (u % 8) ^ swz(row) of that row (rows past
+  // the end clamped): piece q of row r sits at position q ^ ((r / 2) mod 8), which puts the 16 rows
+  // one fragment read serves on 16 different bank groups.
+  const uint16_t* dsrc[16];
   auto dma_rows = [&](int64_t gm0, int gn0) {  // the sources' row starts for a tile (column 0, piece offset)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int r = 16 * (4 * w + j % 4) + lane / 4;
-      const int off = 8 * ((lane % 4) ^ ((r >> 2) & 3));
-      dsrc[j] = j < 4 ? a.x + min<int64_t>(gm0 + r, a.T - 1) * a.hidden + off
+    for (int j = 0; j < 16; ++j) {
+      const int r = 8 * (8 * w + j % 8) + lane / 8;
+      const int off = 8 * ((lane % 8) ^ ((r >> 1) & 7));
+      dsrc[j] = j < 8 ? a.x + min<int64_t>(gm0 + r, a.T - 1) * a.hidden + off
                       : a.w + static_cast<int64_t>(min(gn0 + r, a.width - 1)) * a.hidden + off;
     }
   };
   auto dma = [&](uint4 (&stg)[2][ROWS], int kt) {  // K step kt of the current tile into a stage
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < 16; ++j)
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(dsrc[j] + kt * kProjBK),
-                                       (__attribute__((address_space(3))) void*)(&stg[j / 4][64 * (4 * w + j % 4)]),
+                                       (__attribute__((address_space(3))) void*)(&stg[j / 8][64 * (8 * w + j % 8)]),
                                        16, 0, 0);
   };
 
   // ---- MFMA fragments: step s of a K step, lane l reads piece 2 s + l / 32 of row l mod 32 of a 32-row group
-  const int rr = lane % 32, h = lane / 32, sw = (rr >> 2) & 3;
+  const int rr = lane % 32, h = lane / 32, sw = (rr >> 1) & 7;
   pf32x16_t acc[4][4];  // [packed 32-column tile j][token tile i]
-  uint4 fa[3][4], fb[3][4];  // [0] and [2]: first halves of alternate steps; [1]: second halves
-  // Each lane's fragment offsets are computed once and hidden from the optimiser, so every read of
-  // a stage forms its address the same way: the waitcnt pass then still sees which stage a read
+  uint4 fa[2][4], fb[2][4];  // fragments of alternate sub-steps of 16
+  // Each lane's fragment row offsets are computed once and hidden from the optimiser, so every read
+  // of a stage forms its address the same way: the waitcnt pass then still sees which stage a read
   // comes from (an address merged from two different forms costs a wait for every load in flight)
-  int ia[2], ib[2];
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const int pos = (2 * s + h) ^ sw;
-    ia[s] = (128 * wm + rr) * PIECES + pos;
-    ib[s] = (128 * wn + rr) * PIECES + pos;
-    asm volatile("" : "+v"(ia[s]), "+v"(ib[s]));
-  }
+  int ia = (128 * wm + rr) * PIECES, ib = (128 * wn + rr) * PIECES;
+  asm volatile("" : "+v"(ia), "+v"(ib));
   auto reads = [&](const uint4 (&stg)[2][ROWS], int s, uint4 (&xa)[4], uint4 (&xb)[4]) {
+    const int pos = (2 * s + h) ^ sw;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xa[i] = stg[0][ia[s] + 32 * i * PIECES];
+    for (int i = 0; i < 4; ++i) xa[i] = stg[0][ia + 32 * i * PIECES + pos];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) xb[j] = stg[1][ib[s] + 32 * j * PIECES];
+    for (int j = 0; j < 4; ++j) xb[j] = stg[1][ib + 32 * j * PIECES + pos];
   };
   auto mfmas = [&](const uint4 (&xa)[4], const uint4 (&xb)[4]) {
 #pragma unroll
@@ -178,9 +172,9 @@ __global__ __launch_bounds__(kProjThreads, 1) void proj_qkv_kernel(const ProjArg
                                                             __builtin_bit_cast(pbf16x8_t, xa[i]), acc[j][i], 0, 0, 0);
   };
   // Instruction order inside a K step, one MFMA at a time with the other work between them (the
-  // scheduler is told the pattern, so no burst of reads or loads stalls the matrix unit): the first
-  // half's 16 MFMAs have the second half's 8 fragment reads and the 8 loads of the step three ahead
-  // between them; the second half's 16 MFMAs have the next stage's first 8 fragment reads.
+  // scheduler is told the pattern, so no burst of reads or loads stalls the matrix unit): each
+  // sub-step's 16 MFMAs have the next sub-step's 8 fragment reads between them, and the first
+  // sub-step's also the 16 loads of the next K step.
   auto interleave = [](int reads, int writes, int vloads) {
 #pragma unroll
     for (int m = 0; m < 16; ++m) {
@@ -200,28 +194,24 @@ __global__ __launch_bounds__(kProjThreads, 1) void proj_qkv_kernel(const ProjArg
   int64_t m0 = 0;
   int n0 = 0;
   __syncthreads();     // the epilogue tables above are complete
-  // One K step.  Its fragments of the first half were read during the step before; the second half
-  // is read between the first half's MFMAs, together with the loads of step kt + 3 into the stage
-  // read in the step before (free since the last barrier; past the tile's end they reload its last
-  // step, unused).  The first half of the next stage is read between the second half's MFMAs, so
-  // no read waits on the barrier.  That needs the next stage to be complete one barrier early: the
-  // wait before each barrier leaves only this step's 8 loads per wave in flight, so stage kt + 2
-  // has landed for every wave and a load has two steps to return.  Products only for steps of
-  // the tile.
-  auto step = [&](const uint4 (&cur)[2][ROWS], uint4 (&ahead)[2][ROWS], const uint4 (&next)[2][ROWS], int kt,
-                  uint4 (&a0)[4], uint4 (&b0)[4], uint4 (&a2)[4], uint4 (&b2)[4]) {
+  // One K step: the next K step's loads go to the other stage (its last reads were before the last
+  // barrier; past the tile's end they reload the last step, unused), the four sub-steps of 16 run
+  // from the current stage, then every wave waits for its loads and meets the others at the barrier,
+  // and sub-step 0 of the next stage is read.  Products only for steps of the tile.
+  auto step = [&](const uint4 (&cur)[2][ROWS], uint4 (&nxt)[2][ROWS], int kt) {
     __builtin_amdgcn_sched_barrier(0);
-    reads(cur, 1, fa[1], fb[1]);
-    dma(ahead, min(kt + 3, KT - 1));
-    if (!TAIL || kt < KT) mfmas(a0, b0);
-    interleave(8, 0, 8);
-    __builtin_amdgcn_sched_barrier(0);
-    reads(next, 0, a2, b2);
-    if (!TAIL || kt < KT) mfmas(fa[1], fb[1]);
-    interleave(8, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8) | 8);  // vmcnt <= 8: only this step's loads in flight
+    dma(nxt, min(kt + 1, KT - 1));
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      if (s4 < 3) reads(cur, s4 + 1, fa[(s4 + 1) & 1], fb[(s4 + 1) & 1]);
+      if (!TAIL || kt < KT) mfmas(fa[s4 & 1], fb[s4 & 1]);
+      interleave(s4 < 3 ? 8 : 0, 0, s4 == 0 ? 16 : 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next K step has landed
     __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    reads(nxt, 0, fa[0], fb[0]);
   };
   for (; L < tiles; L += P) {
     tile_of(L, m0, n0);
@@ -232,16 +222,12 @@ __global__ __launch_bounds__(kProjThreads, 1) void proj_qkv_kernel(const ProjArg
       for (int i = 0; i < 4; ++i) acc[j][i] = pf32x16_t{};
     dma_rows(m0, n0);
     dma(lds0, 0);
-    dma(lds1, min(1, KT - 1));
-    dma(lds2, min(2, KT - 1));
-    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8) | 8);  // vmcnt <= 8: steps 0 and 1 have landed
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): step 0 has landed
     __syncthreads();   // for every wave (and the position table is written)
     reads(lds0, 0, fa[0], fb[0]);
     for (int kt = 0; kt < KT; kt += kProjStages) {
-      step(lds0, lds3, lds1, kt, fa[0], fb[0], fa[2], fb[2]);
-      step(lds1, lds0, lds2, kt + 1, fa[2], fb[2], fa[0], fb[0]);
-      step(lds2, lds1, lds3, kt + 2, fa[0], fb[0], fa[2], fb[2]);
-      step(lds3, lds2, lds0, kt + 3, fa[2], fb[2], fa[0], fb[0]);
+      step(lds0, lds1, kt);
+      step(lds1, lds0, kt + 1);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the last loads have landed before LDS is reused
     __syncthreads();
@@ -255,10 +241,10 @@ __global__ __launch_bounds__(kProjThreads, 1) void proj_qkv_kernel(const ProjArg
     // [8 k, 8 k + 8) of a head and their rotate-half partners [D/2 + 8 k, D/2 + 8 k + 8): the sum of
     // squares is a reduction over the G lanes, and cos / sin of the thread's 8 pairs serve every head
     // of the token.
-    // [128][256] fp32, swizzled granules: rows 32 s + [0, 32) in stage array s
+    // [128][256] fp32, swizzled granules: rows 64 s + [0, 64) in stage array s
     auto eprow = [&](int lr) {
-      uint4* base = lr < 64 ? (lr < 32 ? &lds0[0][0] : &lds1[0][0]) : (lr < 96 ? &lds2[0][0] : &lds3[0][0]);
-      return reinterpret_cast<float*>(base) + (lr & 31) * kProjBN;
+      uint4* base = lr < 64 ? &lds0[0][0] : &lds1[0][0];
+      return reinterpret_cast<float*>(base) + (lr & 63) * kProjBN;
     };
     // the q and k weights of the thread's 16 columns, as fp32 (the same for every token)
     float wqv[16], wkv[16];

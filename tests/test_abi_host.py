@@ -344,9 +344,9 @@ def test_proj_forward_argument_checks():
         L = _lay(qk.SECTIONED, T=300, n_kv=8, q_per_kv=4, head_dim=128, rope_dim=128) if L is None else L
         return f(ctypes.byref(L), hidden, x, w, pos, wq, wk, eps, theta, q, k, v, None)
 
-    assert call(hidden=4100) == qk.EINVAL                     # not a multiple of 32
+    assert call(hidden=4100) == qk.EINVAL                     # not a multiple of 64
     assert call(hidden=0) == qk.EINVAL
-    assert call(hidden=16) == qk.EINVAL
+    assert call(hidden=32) == qk.EINVAL
     assert call(hidden=(1 << 30) + 64) == qk.EINVAL
     assert call(L=_lay(qk.LATENT, T=4, width=576, norm_dim=512, rope_dim=64)) == qk.EUNSUPPORTED
     assert call(L=_lay(qk.SECTIONED, dtype=qk.FP32, T=4, n_kv=8, q_per_kv=4, head_dim=128, rope_dim=128)) \

@@ -75,9 +75,9 @@ CASES = [
     ("interleaved", 1, 64, 16, 8, 64, True, "random"),      # one token (decode-like)
     # 8 x 40 = 320 tiles: more than one per persistent workgroup on a 256-CU part, ragged last token tile
     ("interleaved", 2000, 256, 16, 8, 64, True, "random"),
-    ("sectioned", 700, 64, 8, 4, 128, False, "arange"),     # two K steps per tile, several tiles per workgroup
-    ("sectioned", 333, 96, 2, 2, 128, True, "random"),      # three K steps: fewer than the stage count
-    ("interleaved", 40, 32, 1, 2, 64, True, "random"),      # one K step
+    ("sectioned", 700, 64, 8, 4, 128, False, "arange"),     # one K step per tile, several tiles per workgroup
+    ("sectioned", 333, 448, 2, 2, 128, True, "random"),     # seven K steps: not a multiple of the stage count
+    ("interleaved", 40, 320, 1, 2, 64, True, "random"),     # five K steps
 ]
 
 
