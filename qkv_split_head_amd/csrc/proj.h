@@ -92,9 +92,9 @@ template <int D, bool ROPE, bool TAIL>
 __global__ __launch_bounds__(kProjThreads, 1) void proj_qkv_kernel(const ProjArgs a) {
   constexpr int PIECES = kProjBK / 8;       // 16-byte pieces of a row per K step (8)
   constexpr int ROWS = kProjBM * PIECES;    // pieces of one operand tile (2048, 32 KB)
-  // four stages of [x, w][row * 4 + swizzled piece], 32 KB each, as four arrays: with the stage of every
-  // access known at compile time the compiler sees that reading one stage does not touch the others
-  // while their direct-to-LDS loads are in flight
+  // two stages of [x, w][row * 8 + swizzled piece], 64 KB each, as two arrays: with the stage of every
+  // access known at compile time the compiler sees that reading one stage does not touch the other
+  // while its direct-to-LDS loads are in flight
   __shared__ uint4 lds0[2][ROWS], lds1[2][ROWS];
   __shared__ uint16_t ep_w[2][D];           // q and k norm weights, for the epilogue
   __shared__ double ep_turns[D / 2];        // turns per position of each rotate-half pair
