@@ -307,11 +307,12 @@ __global__ __launch_bounds__(kWave * (D / 32), 2) void ns_update_kernel(const ui
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = ld16(xr + static_cast<int64_t>(i) * cols + col);
   };
+  auto dword = [](const uint4& u, int d) { return d == 0 ? u.x : (d == 1 ? u.y : (d == 2 ? u.z : u.w)); };
   auto store_xt = [&](const uint4 (&v)[4], uint4* buf) {
     const int k = 4 * rg;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {  // dword d of a row holds columns 2 d (low half) and 2 d + 1
-      const uint32_t a0 = (&v[0].x)[d], a1 = (&v[1].x)[d], a2 = (&v[2].x)[d], a3 = (&v[3].x)[d];
+      const uint32_t a0 = dword(v[0], d), a1 = dword(v[1], d), a2 = dword(v[2], d), a3 = dword(v[3], d);
       const uint2 lo = make_uint2((a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16));
       const uint2 hi = make_uint2((a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u));
       const int n0 = 8 * cg + 2 * d, n1 = n0 + 1;
