@@ -65,7 +65,7 @@ extern "C" {
 #define QKVNR_OK 0
 #define QKVNR_EINVAL (-1)      /* a null pointer, a bad size, or a width that is not the exact total */
 #define QKVNR_EALIGN (-2)      /* a pointer or the input row stride is not aligned as required */
-#define QKVNR_EUNSUPPORTED (-3)/* a shape this build has no kernel for, or no gfx950 device current */
+#define QKVNR_EUNSUPPORTED (-3)/* a shape the library has no kernel for, or no gfx950 device current */
 #define QKVNR_EHIP (-4)        /* a HIP runtime call or launch failed; qkvnr_strerror has its text */
 
 /* Packed layouts. */
