@@ -94,6 +94,19 @@ def test_fused_projection_matches_the_oracle(kind, T, hidden, n_kv, q_per_kv, D,
         assert_close(got, r, "bf16", what)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_fused_projection_at_positions_near_int32_max(D):
+    # the angle is formed and reduced in fp64 turns: positions up to 2^31 - 1 keep the 2-ulp bound
+    inp = projection("interleaved", 96, 128, 2, 2, D, theta=1e6 if D == 128 else 5e5, positions="random",
+                     max_pos=2 ** 31 - 1, seed=95 + D)
+    assert int(inp.positions.max()) > 2 ** 30
+    q, k, v = _run(inp)
+    ref = projected_forward_gqa(inp.x, inp.w_qkv, "interleaved", 2, 2, D, inp.positions, inp.q_norm_w, inp.k_norm_w,
+                                inp.eps, inp.theta, rope=True)
+    for got, r, what in zip((q, k, v), ref, "qkv"):
+        assert_close(got, r, "bf16", what)
+
+
 def _val(bits):
     return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
