@@ -71,7 +71,7 @@ __global__ __launch_bounds__(kWave * (D / 32)) void gram_partials_kernel(const u
     slot[j] = r * PIECES + (q ^ ((r >> 1) & 7));
   }
   auto load = [&](int c, uint4 (&v)[PER]) {
-    const int col = min(k0 + c * kGramChunk + 8 * q, cols - 8);  // clamped into the row
+    const int col = min(k0 + c * kGramChunk + 8 * q, kend - 8);  // past the slice: its last columns again (cached)
 #pragma unroll
     for (int j = 0; j < PER; ++j) v[j] = ld16(rp[j] + col);
   };
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(kWave * (D / 32), 2) void ns_update_kernel(const ui
   const int rg = threadIdx.x / 8, cg = threadIdx.x % 8;
   const uint16_t* xr = x + (blk * D + 4 * rg) * static_cast<int64_t>(cols);
   auto load = [&](int c, uint4 (&v)[4]) {
-    const int col = min(k0 + c * kGramChunk + 8 * cg, cols - 8);  // clamped into the row
+    const int col = min(k0 + c * kGramChunk + 8 * cg, kend - 8);  // past the slice: its last columns again (cached)
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = ld16(xr + static_cast<int64_t>(i) * cols + col);
   };
