@@ -127,6 +127,41 @@ def _stream(stream) -> Optional[int]:
     return stream if isinstance(stream, int) else stream.cuda_stream
 
 
+def _need(t, name: str, *, device: Optional[torch.device] = None, dtype=None, shape=None,
+          contiguous: bool = True) -> None:
+    """Checks a tensor argument of the tensor-level wrappers before its address reaches a kernel.
+
+    The C ABI sees plain pointers and cannot tell a host address, a wrong
+    element type or a buffer too small for the sizes it is given; these
+    wrappers know the shapes, so they reject such arguments here.  ``device``
+    None means the current GPU.
+    """
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor, not {type(t).__name__}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} is on {t.device}; the library's kernels need GPU tensors")
+    want = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    if t.device != want:
+        raise ValueError(f"{name} is on {t.device}; it must be on {want} (the current GPU)")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _need_inputs(x: torch.Tensor, positions, q_norm_w, k_norm_w, head_dim: int, need_pos: bool) -> None:
+    """positions int32 [T] and norm weights [head_dim] of x's dtype, all on x's (current) device."""
+    _need(x, "the packed input", contiguous=False)
+    T = x.shape[0]
+    if positions is not None or need_pos:
+        _need(positions, "positions", device=x.device, dtype=torch.int32, shape=(T,))
+    for w, nm in ((q_norm_w, "q_norm_w"), (k_norm_w, "k_norm_w")):
+        if w is not None:
+            _need(w, nm, device=x.device, dtype=x.dtype, shape=(head_dim,))
+
+
 # ------------------------------------------------------------------ raw entry points
 
 
@@ -258,6 +293,7 @@ def forward(qkv: torch.Tensor, positions: Optional[torch.Tensor], q_norm_w: torc
             stream=None):
     """Split + q/k RMSNorm + RoPE + v copy; returns contiguous (q [T,n_q,D], k [T,n_kv,D], v [T,n_kv,D])."""
     L = gqa_layout(qkv, kind, n_kv, q_per_kv, head_dim, rope)
+    _need_inputs(qkv, positions, q_norm_w, k_norm_w, head_dim, rope)
     T = qkv.shape[0]
     if out is None:
         q = torch.empty((T, n_kv * q_per_kv, head_dim), dtype=qkv.dtype, device=qkv.device)
@@ -265,6 +301,9 @@ def forward(qkv: torch.Tensor, positions: Optional[torch.Tensor], q_norm_w: torc
         v = torch.empty((T, n_kv, head_dim), dtype=qkv.dtype, device=qkv.device)
     else:
         q, k, v = out
+        _need(q, "q", device=qkv.device, dtype=qkv.dtype, shape=(T, n_kv * q_per_kv, head_dim))
+        _need(k, "k", device=qkv.device, dtype=qkv.dtype, shape=(T, n_kv, head_dim))
+        _need(v, "v", device=qkv.device, dtype=qkv.dtype, shape=(T, n_kv, head_dim))
     qkvnr_forward(L, qkv, positions, q_norm_w, k_norm_w, eps, theta, q, k, v, stream)
     return q, k, v
 
@@ -275,16 +314,41 @@ def backward(qkv: torch.Tensor, positions: Optional[torch.Tensor], q_norm_w: tor
              workspace: Optional[torch.Tensor] = None, stream=None):
     """Packed dqkv (input layout) and fp32 norm-weight grads (dq_norm_w, dk_norm_w)."""
     L = gqa_layout(qkv, kind, n_kv, q_per_kv, head_dim, rope)
+    _need_inputs(qkv, positions, q_norm_w, k_norm_w, head_dim, rope)
+    T, n_q = qkv.shape[0], n_kv * q_per_kv
+    _need(dq, "dq", device=qkv.device, dtype=qkv.dtype, shape=(T, n_q, head_dim))
+    _need(dk, "dk", device=qkv.device, dtype=qkv.dtype, shape=(T, n_kv, head_dim))
+    _need(dv, "dv", device=qkv.device, dtype=qkv.dtype, shape=(T, n_kv, head_dim))
     if out is None:
         dqkv = torch.empty_strided(qkv.shape, qkv.stride(), dtype=qkv.dtype, device=qkv.device)
         dwq = torch.empty(head_dim, dtype=torch.float32, device=qkv.device)
         dwk = torch.empty(head_dim, dtype=torch.float32, device=qkv.device)
     else:
         dqkv, dwq, dwk = out
+        _need(dqkv, "dqkv", device=qkv.device, dtype=qkv.dtype, shape=qkv.shape, contiguous=False)
+        if T > 1 and dqkv.stride(0) != qkv.stride(0):   # written with the input's row stride
+            raise ValueError(f"dqkv has row stride {dqkv.stride(0)}, the packed input {qkv.stride(0)}")
+        if T > 0 and not dqkv[0].is_contiguous():
+            raise ValueError("the values of a dqkv row must be dense")
+        _need(dwq, "dq_norm_w", device=qkv.device, dtype=torch.float32, shape=(head_dim,))
+        _need(dwk, "dk_norm_w", device=qkv.device, dtype=torch.float32, shape=(head_dim,))
     ws = backward_workspace(qkv.device) if workspace is None else workspace
+    _need(ws, "workspace", device=qkv.device)
     qkvnr_backward(L, qkv, positions, q_norm_w, k_norm_w, eps, theta, dq, dk, dv, dqkv, dwq, dwk, ws,
                    ws.numel() * ws.element_size(), stream)
     return dqkv, dwq, dwk
+
+
+def _need_table(block_table, device: torch.device, T: int, tokens_per_req: int) -> None:
+    """int32 block table with a row for every request of the batch (T / tokens_per_req, rounded up)."""
+    _need(block_table, "block_table", device=device, dtype=torch.int32)
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [requests, pages per request]")
+    if tokens_per_req < 1:
+        raise ValueError("tokens_per_req must be >= 1")
+    if block_table.shape[0] < -(-T // tokens_per_req):
+        raise ValueError(f"block_table has {block_table.shape[0]} rows; {T} tokens of {tokens_per_req} per "
+                         f"request need {-(-T // tokens_per_req)}")
 
 
 def forward_paged(qkv, positions, q_norm_w, k_norm_w, block_table: torch.Tensor, k_pool: torch.Tensor,
@@ -293,12 +357,29 @@ def forward_paged(qkv, positions, q_norm_w, k_norm_w, block_table: torch.Tensor,
                   q: Optional[torch.Tensor] = None, stream=None):
     """GQA forward with k/v stored into pools [num_pages, page_size, n_kv, D]; returns q."""
     L = gqa_layout(qkv, kind, n_kv, q_per_kv, head_dim, rope)
-    if q is None:
-        q = torch.empty((qkv.shape[0], n_kv * q_per_kv, head_dim), dtype=qkv.dtype, device=qkv.device)
+    _need_inputs(qkv, positions, q_norm_w, k_norm_w, head_dim, rope)
+    T = qkv.shape[0]
+    _need_table(block_table, qkv.device, T, tokens_per_req)
+    if k_pool.dim() != 4:
+        raise ValueError("k_pool must be [num_pages, page_size, n_kv, head_dim]")
     num_pages, page_size = k_pool.shape[0], k_pool.shape[1]
+    _need(k_pool, "k_pool", device=qkv.device, dtype=qkv.dtype, shape=(num_pages, page_size, n_kv, head_dim))
+    _need(v_pool, "v_pool", device=qkv.device, dtype=qkv.dtype, shape=(num_pages, page_size, n_kv, head_dim))
+    if q is None:
+        q = torch.empty((T, n_kv * q_per_kv, head_dim), dtype=qkv.dtype, device=qkv.device)
+    else:
+        _need(q, "q", device=qkv.device, dtype=qkv.dtype, shape=(T, n_kv * q_per_kv, head_dim))
     qkvnr_forward_paged(L, qkv, positions, q_norm_w, k_norm_w, eps, theta, block_table, block_table.shape[1],
                         tokens_per_req, page_size, num_pages, q, k_pool, v_pool, stream)
     return q
+
+
+def _need_latent(rows: torch.Tensor, positions, norm_w, norm_dim: int) -> None:
+    _need(rows, "rows", contiguous=False)
+    if rows.dtype not in DTYPES:
+        raise TypeError(f"rows dtype {rows.dtype} is not bf16 or fp32")
+    _need(positions, "positions", device=rows.device, dtype=torch.int32, shape=(rows.shape[0],))
+    _need(norm_w, "norm_w", device=rows.device, dtype=rows.dtype, shape=(norm_dim,))
 
 
 def forward_latent(rows: torch.Tensor, positions: torch.Tensor, norm_w: torch.Tensor, *, eps: float = 1e-6,
@@ -306,8 +387,11 @@ def forward_latent(rows: torch.Tensor, positions: torch.Tensor, norm_w: torch.Te
                    out: Optional[torch.Tensor] = None, stream=None):
     """Latent rows [T, norm_dim + rope_dim] -> [RMSNorm(head) || RoPE(tail)], contiguous."""
     L = latent_layout(rows, norm_dim, rope_dim)
+    _need_latent(rows, positions, norm_w, norm_dim)
     if out is None:
         out = torch.empty((rows.shape[0], norm_dim + rope_dim), dtype=rows.dtype, device=rows.device)
+    else:
+        _need(out, "out", device=rows.device, dtype=rows.dtype, shape=(rows.shape[0], norm_dim + rope_dim))
     qkvnr_forward(L, rows, positions, None, norm_w, eps, theta, None, out, None, stream)
     return out
 
@@ -318,6 +402,11 @@ def forward_latent_paged(rows: torch.Tensor, positions: torch.Tensor, norm_w: to
                          stream=None) -> None:
     """Latent rows stored straight into pool [num_pages, page_size, norm_dim + rope_dim]."""
     L = latent_layout(rows, norm_dim, rope_dim)
+    _need_latent(rows, positions, norm_w, norm_dim)
+    _need_table(block_table, rows.device, rows.shape[0], tokens_per_req)
+    if pool.dim() != 3:
+        raise ValueError("pool must be [num_pages, page_size, norm_dim + rope_dim]")
+    _need(pool, "pool", device=rows.device, dtype=rows.dtype, shape=(pool.shape[0], pool.shape[1], norm_dim + rope_dim))
     qkvnr_forward_paged(L, rows, positions, None, norm_w, eps, theta, block_table, block_table.shape[1],
                         tokens_per_req, pool.shape[1], pool.shape[0], None, pool, None, stream)
 
@@ -330,6 +419,11 @@ def rope_inplace(x: torch.Tensor, positions: torch.Tensor, *, rope_offset: int, 
         raise ValueError("x must be [T, heads, head_stride] with a contiguous last dimension")
     if x.dtype not in DTYPES:
         raise ValueError(f"unsupported dtype {x.dtype}")
+    _need(x, "x", contiguous=False)
+    _need(positions, "positions", device=x.device, dtype=torch.int32, shape=(x.shape[0],))
+    if rope_offset < 0 or rope_dim < 0 or rope_offset + rope_dim > x.shape[2]:
+        raise ValueError(f"rotated span [{rope_offset}, {rope_offset + rope_dim}) is outside the {x.shape[2]} "
+                         "values of a head")
     qkvnr_rope_inplace(DTYPES[x.dtype], x.shape[0], x.shape[1], x.stride(0), x.stride(1), rope_offset, rope_dim,
                        positions, theta, x, stream)
     return x
@@ -351,6 +445,9 @@ def proj_forward(x: torch.Tensor, w_qkv: torch.Tensor, positions: Optional[torch
     width = (n_kv * q_per_kv + 2 * n_kv) * head_dim
     if w_qkv.shape[1] != hidden:
         raise ValueError(f"w_qkv has {w_qkv.shape[1]} columns, x has {hidden}")
+    _need(x, "x")
+    _need(w_qkv, "w_qkv", device=x.device, dtype=x.dtype)
+    _need_inputs(x, positions, q_norm_w, k_norm_w, head_dim, rope)
     L = Layout(kind=KINDS[kind], dtype=DTYPES[x.dtype], T=T, n_kv=n_kv, q_per_kv=q_per_kv, head_dim=head_dim,
                rope_dim=head_dim if rope else 0, norm_dim=0, reserved=0, width=w_qkv.shape[0], in_row_stride=width)
     if out is None:
@@ -359,5 +456,8 @@ def proj_forward(x: torch.Tensor, w_qkv: torch.Tensor, positions: Optional[torch
         v = torch.empty((T, n_kv, head_dim), dtype=x.dtype, device=x.device)
     else:
         q, k, v = out
+        _need(q, "q", device=x.device, dtype=x.dtype, shape=(T, n_kv * q_per_kv, head_dim))
+        _need(k, "k", device=x.device, dtype=x.dtype, shape=(T, n_kv, head_dim))
+        _need(v, "v", device=x.device, dtype=x.dtype, shape=(T, n_kv, head_dim))
     qkvnr_proj_forward(L, hidden, x, w_qkv, positions, q_norm_w, k_norm_w, eps, theta, q, k, v, stream)
     return q, k, v

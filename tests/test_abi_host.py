@@ -364,3 +364,26 @@ def test_proj_forward_argument_checks():
     # NoPE: positions may be NULL (the call then fails only for want of a device here)
     nope = _lay(qk.INTERLEAVED, T=0, n_kv=2, q_per_kv=4, head_dim=64, rope_dim=0)
     assert call(L=nope, pos=None, x=0, w=0, q=0, k=0, v=0) == qk.OK   # T == 0 enqueues nothing
+
+
+def test_tensor_wrappers_reject_host_tensors_before_any_call():
+    """The tensor-level wrappers refuse host tensors themselves: their addresses never reach the C ABI."""
+    import torch
+    T, n_kv, Q, D = 4, 2, 2, 64
+    qkv = torch.zeros((T, n_kv, Q + 2, D), dtype=torch.bfloat16)
+    pos = torch.zeros(T, dtype=torch.int32)
+    w = torch.ones(D, dtype=torch.bfloat16)
+    kw = dict(kind="interleaved", n_kv=n_kv, q_per_kv=Q, head_dim=D)
+    with pytest.raises(ValueError, match="need GPU tensors"):
+        qk.forward(qkv, pos, w, w, **kw)
+    g = torch.zeros((T, n_kv * Q, D), dtype=torch.bfloat16)
+    gk = torch.zeros((T, n_kv, D), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="need GPU tensors"):
+        qk.backward(qkv, pos, w, w, g, gk, gk, **kw)
+    rows = torch.zeros((T, 576), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="need GPU tensors"):
+        qk.forward_latent(rows, pos, torch.ones(512, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="need GPU tensors"):
+        qk.rope_inplace(torch.zeros((T, 2, 64), dtype=torch.bfloat16), pos, rope_offset=0)
+    with pytest.raises(TypeError, match="must be a torch tensor"):
+        qk._binding._need(None, "positions")

@@ -219,6 +219,36 @@ def test_forward_rejects_misaligned_device_pointer():
     assert ei.value.code == qk.EALIGN
 
 
+
+def test_wrappers_refuse_mismatched_tensors():
+    """Outputs of the wrong shape, positions of the wrong type and a block table with too few rows are
+    refused by the tensor-level wrappers, before any kernel could write past a buffer."""
+    w = custom_gqa("interleaved", "bf16", 8, 2, 2, 64, seed=3, grads=True)
+    qkv, pos = to_dev(w.qkv, "bf16"), to_dev(w.positions, "int32")
+    wq, wk = to_dev(w.q_norm_w, "bf16"), to_dev(w.k_norm_w, "bf16")
+    kw = dict(kind="interleaved", n_kv=2, q_per_kv=2, head_dim=64, eps=w.eps, theta=w.theta)
+    q, k, v = qk.forward(qkv, pos, wq, wk, **kw)
+    with pytest.raises(ValueError, match="shape"):
+        qk.forward(qkv, pos, wq, wk, out=(q[:4], k, v), **kw)
+    with pytest.raises(TypeError, match="dtype"):
+        qk.forward(qkv, pos.long(), wq, wk, **kw)
+    with pytest.raises(TypeError, match="dtype"):
+        qk.forward(qkv, pos, wq.float(), wk, **kw)
+    dq, dk, dv = to_dev(w.dq, "bf16"), to_dev(w.dk, "bf16"), to_dev(w.dv, "bf16")
+    with pytest.raises(ValueError, match="shape"):
+        qk.backward(qkv, pos, wq, wk, dq[:2], dk, dv, **kw)
+    dqkv, dwq, dwk = qk.backward(qkv, pos, wq, wk, dq, dk, dv, **kw)
+    with pytest.raises(ValueError, match="shape"):
+        qk.backward(qkv, pos, wq, wk, dq, dk, dv, out=(dqkv, dwq[:32], dwk), **kw)
+    kp = torch.zeros((4, 16, 2, 64), dtype=torch.bfloat16, device="cuda")
+    bt = torch.zeros((1, 4), dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError, match="block_table has 1 rows"):
+        qk.forward_paged(qkv, pos, wq, wk, bt, kp, kp.clone(), tokens_per_req=4, **kw)
+    with pytest.raises(ValueError, match="shape"):
+        qk.forward_paged(qkv, pos, wq, wk, bt, kp, kp[:, :8], tokens_per_req=8, **kw)
+    torch.cuda.synchronize()
+
+
 # ------------------------------------------------------------------ GPU-vs-GPU bitwise equivalences
 
 
