@@ -82,6 +82,7 @@ def per_head_newton_schulz(G: torch.Tensor, n_q: int, n_kv: int, head_dim: int, 
     """
     if G.dim() != 2:
         raise ValueError("G must be a 2-D weight")
+    b._need(G, "G", contiguous=False)   # the kernels take device addresses: a host weight is refused here
     rows, cols = G.shape
     nb = fused_head_blocks(n_q, n_kv, head_dim, rows)
     dt = G.dtype if compute_dtype is None else compute_dtype

@@ -385,5 +385,8 @@ def test_tensor_wrappers_reject_host_tensors_before_any_call():
         qk.forward_latent(rows, pos, torch.ones(512, dtype=torch.bfloat16))
     with pytest.raises(ValueError, match="need GPU tensors"):
         qk.rope_inplace(torch.zeros((T, 2, 64), dtype=torch.bfloat16), pos, rope_offset=0)
+    from qkv_split_head_amd.muon import per_head_newton_schulz
+    with pytest.raises(ValueError, match="need GPU tensors"):
+        per_head_newton_schulz(torch.zeros((12 * 64, 256), dtype=torch.bfloat16), 8, 2, 64)
     with pytest.raises(TypeError, match="must be a torch tensor"):
         qk._binding._need(None, "positions")
