@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define QKVNR_VERSION 10300 /* major * 10000 + minor * 100 + patch */
+#define QKVNR_VERSION 10301 /* major * 10000 + minor * 100 + patch */
 
 /* Return codes. */
 #define QKVNR_OK 0
@@ -251,7 +251,7 @@ int qkvnr_fused_head_blocks(int32_t n_q, int32_t n_kv, int32_t head_dim, int64_t
  * the first product of each Newton-Schulz step (and G G^T for the first).
  * Both factors are rows of X, read along the long side; v_mfma_f32_32x32x16_bf16.
  *
- *   blocks  number of blocks, 0 .. 2^31 - 1 (0 is a no-op).
+ *   blocks  number of blocks, 0 .. 2^22 (0 is a no-op).
  *   d       block side (rows of each block): 32, 64, 96 or 128 (others
  *           QKVNR_EUNSUPPORTED).
  *   cols    block width, a positive multiple of 8 (QKVNR_EALIGN otherwise), at
@@ -278,7 +278,7 @@ int qkvnr_gram_partials(int64_t blocks, int32_t d, int64_t cols, const void* x, 
  * GEMM).
  *
  *   dtype   QKVNR_BF16 or QKVNR_FP32: the type of p.
- *   blocks  number of blocks, >= 0 (0 is a no-op).
+ *   blocks  number of blocks, 0 .. 2^22 (0 is a no-op).
  *   d       block side, 1..128 (others QKVNR_EUNSUPPORTED).
  *   gram    [blocks, parts, d, d] fp32, row-major, 16-byte aligned; read
  *           only (the partials are added in order as they are loaded).
@@ -295,7 +295,7 @@ int qkvnr_ns_poly(int32_t dtype, int64_t blocks, int32_t d, float* gram, int32_t
  * once and not read back.  (DeepSpeed page, "What this PR does": each head
  * block is orthogonalised on its own; every step is X <- P X.)
  *
- *   blocks  number of blocks, 0 .. 2^31 - 1 (0 is a no-op).
+ *   blocks  number of blocks, 0 .. 2^22 (0 is a no-op).
  *   d       block side: 64 or 128 (others QKVNR_EUNSUPPORTED).
  *   cols    block width, a positive multiple of 8 (QKVNR_EALIGN otherwise), at
  *           most 2^30 (QKVNR_EINVAL otherwise).

@@ -16,6 +16,7 @@ from .generators import (  # noqa: F401
     latent_paged,
     gqa_paged,
     custom_gqa,
+    token_positions,
     MlaDrafterInputs,
     mla_drafter_layer,
     SEEDS,

@@ -180,6 +180,17 @@ def train_sectioned(T: int = 16384, grads: bool = True) -> Workload:
                       name=f"qwen3_8b_train_T{T}")
 
 
+def token_positions(T: int, seed: int, high: int = 2**31 - 1) -> np.ndarray:
+    """T int32 positions drawn uniformly from [0, high).
+
+    For batches too large to draw row by row: their packed rows are a smaller
+    draw repeated, and each token still gets a position of its own, so no two
+    tokens see the same rotation.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return rng.integers(0, high, size=T, dtype=np.int64).astype(np.int32)
+
+
 def _block_table(rng, B, T_req, num_pages, page_size, ctx_lo, ctx_hi):
     """Context lengths, draft-token positions and a non-overlapping block table.
 

@@ -94,6 +94,7 @@ struct GqaArgs {
   float inv_d;
   int64_t T;
   int64_t units;        // T * units_per_token
+  int64_t unit0;        // first work unit of this launch (a large batch takes several launches)
   uint64_t upt_magic;   // ceil(2^64 / upt) for upt > 1: unit / upt = umul64hi(unit, magic)
   int32_t upt;          // work units per token
   int32_t kind;
@@ -168,7 +169,7 @@ struct Geo {
 // This wave's work unit: token t and its first iteration it0 (wave-uniform).
 __device__ __forceinline__ bool wave_unit(const GqaArgs& a, int U, int waves_per_block, int64_t& t, int& it0) {
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-  const int64_t unit = static_cast<int64_t>(blockIdx.x) * waves_per_block + wave;
+  const int64_t unit = a.unit0 + static_cast<int64_t>(blockIdx.x) * waves_per_block + wave;
   if (unit >= a.units) return false;
   t = a.upt == 1 ? unit  // one unit per token: no division (and no 2^64 magic)
                  : static_cast<int64_t>(__umul64hi(static_cast<uint64_t>(unit), a.upt_magic));
@@ -533,6 +534,7 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_latent_kernel(const LatentA
 struct RopeArgs {
   uint8_t* x;
   int64_t T;
+  int64_t t0;  // first token of this launch (a large batch takes several launches)
   int64_t token_bytes;
   int32_t head_bytes;
   int32_t rope_off_bytes;
@@ -550,7 +552,7 @@ __global__ __launch_bounds__(kBlockThreads) void rope_inplace_kernel(const RopeA
   const int hs = lane / LPH;
   const int c = chunk_of_lane<LPH>(li);
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave;
+  const int64_t t = a.t0 + static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave;
   if (t >= a.T) return;  // wave-uniform
   const double tpp = a.turns[lane % (R / 2)];
   const int32_t p = a.pos[t];

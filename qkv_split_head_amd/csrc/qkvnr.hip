@@ -217,8 +217,23 @@ void plan_gqa(GqaArgs& a, const qkvnr_layout* L, int U, double theta) {
 #define QKVNR_BWD_LDS 0
 #endif
 
-int unit_grid(const GqaArgs& a, int waves_per_block) {
-  return static_cast<int>((a.units + waves_per_block - 1) / waves_per_block);
+// Blocks per launch.  A dispatch holds fewer than 2^32 work-items, so a batch with more blocks
+// (for instance 2^24 tokens of a few small heads) is launched in pieces of this many blocks,
+// each piece told its first work unit (or token).
+constexpr int64_t kMaxLaunchBlocks = int64_t(1) << 22;
+
+// Launches launch(grid) once per piece of at most kMaxLaunchBlocks blocks over `items` work
+// items of `per_block` per block, after set_first(first item of the piece); stops at the first
+// launch that fails.
+template <typename SetFirst, typename Launch>
+int launch_pieces(int64_t items, int per_block, const char* what, SetFirst&& set_first, Launch&& launch) {
+  const int64_t blocks = (items + per_block - 1) / per_block;
+  for (int64_t b0 = 0; b0 < blocks; b0 += kMaxLaunchBlocks) {
+    set_first(b0 * per_block);
+    launch(dim3(static_cast<uint32_t>(std::min(kMaxLaunchBlocks, blocks - b0))));
+    if (int rc = launched(what)) return rc;
+  }
+  return QKVNR_OK;
 }
 
 // Below this many work units of kFwdU iterations (8 waves per CU of the
@@ -226,31 +241,37 @@ int unit_grid(const GqaArgs& a, int waves_per_block) {
 constexpr int64_t kSmallBatchUnits = 2048;
 
 template <bool PAGED, int U, int DEPTH>
-void launch_fwd_gqa(const GqaArgs& a, int32_t dtype, int32_t D, bool rope, hipStream_t s) {
-  const dim3 g(unit_grid(a, kWavesPerBlock)), b(kBlockThreads);
+int launch_fwd_gqa(GqaArgs a, int32_t dtype, int32_t D, bool rope, hipStream_t s) {
+  const dim3 b(kBlockThreads);
+  auto launch = [&](dim3 g) {
 #define QKVNR_FWD(IO, DD, R) \
   hipLaunchKernelGGL((fwd_gqa_kernel<IO, DD, R, PAGED, U, DEPTH>), g, b, QKVNR_FWD_LDS, s, a)
-  if (dtype == QKVNR_BF16) {
-    if (D == 64) { if (rope) QKVNR_FWD(uint16_t, 64, true); else QKVNR_FWD(uint16_t, 64, false); }
-    else         { if (rope) QKVNR_FWD(uint16_t, 128, true); else QKVNR_FWD(uint16_t, 128, false); }
-  } else {
-    if (D == 64) { if (rope) QKVNR_FWD(float, 64, true); else QKVNR_FWD(float, 64, false); }
-    else         { if (rope) QKVNR_FWD(float, 128, true); else QKVNR_FWD(float, 128, false); }
-  }
+    if (dtype == QKVNR_BF16) {
+      if (D == 64) { if (rope) QKVNR_FWD(uint16_t, 64, true); else QKVNR_FWD(uint16_t, 64, false); }
+      else         { if (rope) QKVNR_FWD(uint16_t, 128, true); else QKVNR_FWD(uint16_t, 128, false); }
+    } else {
+      if (D == 64) { if (rope) QKVNR_FWD(float, 64, true); else QKVNR_FWD(float, 64, false); }
+      else         { if (rope) QKVNR_FWD(float, 128, true); else QKVNR_FWD(float, 128, false); }
+    }
 #undef QKVNR_FWD
+  };
+  return launch_pieces(a.units, kWavesPerBlock, "forward", [&](int64_t u0) { a.unit0 = u0; }, launch);
 }
 
-void launch_bwd_gqa(const GqaArgs& a, int32_t dtype, int32_t D, bool rope, hipStream_t s) {
-  const dim3 g(unit_grid(a, kBwdWavesPerBlock)), b(kBwdBlockThreads);
+int launch_bwd_gqa(GqaArgs a, int32_t dtype, int32_t D, bool rope, hipStream_t s) {
+  const dim3 b(kBwdBlockThreads);
+  auto launch = [&](dim3 g) {
 #define QKVNR_BWD(IO, DD, R) hipLaunchKernelGGL((bwd_gqa_kernel<IO, DD, R>), g, b, QKVNR_BWD_LDS, s, a)
-  if (dtype == QKVNR_BF16) {
-    if (D == 64) { if (rope) QKVNR_BWD(uint16_t, 64, true); else QKVNR_BWD(uint16_t, 64, false); }
-    else         { if (rope) QKVNR_BWD(uint16_t, 128, true); else QKVNR_BWD(uint16_t, 128, false); }
-  } else {
-    if (D == 64) { if (rope) QKVNR_BWD(float, 64, true); else QKVNR_BWD(float, 64, false); }
-    else         { if (rope) QKVNR_BWD(float, 128, true); else QKVNR_BWD(float, 128, false); }
-  }
+    if (dtype == QKVNR_BF16) {
+      if (D == 64) { if (rope) QKVNR_BWD(uint16_t, 64, true); else QKVNR_BWD(uint16_t, 64, false); }
+      else         { if (rope) QKVNR_BWD(uint16_t, 128, true); else QKVNR_BWD(uint16_t, 128, false); }
+    } else {
+      if (D == 64) { if (rope) QKVNR_BWD(float, 64, true); else QKVNR_BWD(float, 64, false); }
+      else         { if (rope) QKVNR_BWD(float, 128, true); else QKVNR_BWD(float, 128, false); }
+    }
 #undef QKVNR_BWD
+  };
+  return launch_pieces(a.units, kBwdWavesPerBlock, "backward", [&](int64_t u0) { a.unit0 = u0; }, launch);
 }
 
 constexpr int kLatentBlocksPerCu = 8;
@@ -335,13 +356,11 @@ int gqa_forward(const qkvnr_layout* L, const void* qkv, const int32_t* positions
   a.page_size = page_size;
   a.num_pages = num_pages;
   if (paged) {
-    if (small) launch_fwd_gqa<true, 1, 1>(a, L->dtype, L->head_dim, rope, stream);
-    else launch_fwd_gqa<true, kFwdU, kFwdDepth>(a, L->dtype, L->head_dim, rope, stream);
-  } else {
-    if (small) launch_fwd_gqa<false, 1, 1>(a, L->dtype, L->head_dim, rope, stream);
-    else launch_fwd_gqa<false, kFwdU, kFwdDepth>(a, L->dtype, L->head_dim, rope, stream);
+    if (small) return launch_fwd_gqa<true, 1, 1>(a, L->dtype, L->head_dim, rope, stream);
+    return launch_fwd_gqa<true, kFwdU, kFwdDepth>(a, L->dtype, L->head_dim, rope, stream);
   }
-  return launched("forward");
+  if (small) return launch_fwd_gqa<false, 1, 1>(a, L->dtype, L->head_dim, rope, stream);
+  return launch_fwd_gqa<false, kFwdU, kFwdDepth>(a, L->dtype, L->head_dim, rope, stream);
 }
 
 template <int D, bool ROPE>
@@ -453,8 +472,7 @@ int qkvnr_backward(const qkvnr_layout* layout, const void* qkv, const int32_t* p
   a.dwk = dk_norm_w;
   a.slots = static_cast<float*>(workspace);
   a.eps = eps;
-  launch_bwd_gqa(a, L->dtype, L->head_dim, rope, stream);
-  if (int rc = launched("backward")) return rc;
+  if (int rc = launch_bwd_gqa(a, L->dtype, L->head_dim, rope, stream)) return rc;
   if (D == 64)
     hipLaunchKernelGGL(wgrad_fold_kernel<64>, dim3(1), dim3(kFoldThreads), 0, stream, a.slots, dq_norm_w, dk_norm_w);
   else
@@ -498,12 +516,15 @@ int qkvnr_rope_inplace(int32_t dtype, int64_t T, int32_t heads, int64_t token_st
   a.iters = (heads + hpi - 1) / hpi;
   a.pos = positions;
   fill_turns(a.turns, theta, rope_dim);
-  const dim3 g(static_cast<uint32_t>((T + kWavesPerBlock - 1) / kWavesPerBlock)), b(kBlockThreads);
-  if (rope_dim == 64)
-    hipLaunchKernelGGL(rope_inplace_kernel<64>, g, b, 0, stream, a);
-  else
-    hipLaunchKernelGGL(rope_inplace_kernel<128>, g, b, 0, stream, a);
-  return launched("rope in place");
+  const dim3 b(kBlockThreads);
+  return launch_pieces(
+      T, kWavesPerBlock, "rope in place", [&](int64_t t0) { a.t0 = t0; },
+      [&](dim3 g) {
+        if (rope_dim == 64)
+          hipLaunchKernelGGL(rope_inplace_kernel<64>, g, b, 0, stream, a);
+        else
+          hipLaunchKernelGGL(rope_inplace_kernel<128>, g, b, 0, stream, a);
+      });
 }
 
 int qkvnr_fused_head_blocks(int32_t n_q, int32_t n_kv, int32_t head_dim, int64_t weight_rows, int64_t* blocks) {
@@ -521,7 +542,8 @@ int qkvnr_fused_head_blocks(int32_t n_q, int32_t n_kv, int32_t head_dim, int64_t
 
 int qkvnr_gram_partials(int64_t blocks, int32_t d, int64_t cols, const void* x, int32_t parts, float* out,
                         hipStream_t stream) {
-  if (blocks < 0 || blocks > INT32_MAX) return fail(QKVNR_EINVAL, "blocks %lld out of [0, 2^31)", (long long)blocks);
+  if (blocks < 0 || blocks > kMaxLaunchBlocks)  // one launch, one workgroup (row) per block
+    return fail(QKVNR_EINVAL, "blocks %lld out of [0, 2^22]", (long long)blocks);
   if (d != 32 && d != 64 && d != 96 && d != 128)
     return fail(QKVNR_EUNSUPPORTED, "block side %d: kernels exist for 32, 64, 96 and 128", d);
   if (cols < 1 || cols % 8) return fail(QKVNR_EALIGN, "cols %lld must be a positive multiple of 8", (long long)cols);
@@ -554,7 +576,8 @@ int qkvnr_gram_partials(int64_t blocks, int32_t d, int64_t cols, const void* x, 
 int qkvnr_ns_poly(int32_t dtype, int64_t blocks, int32_t d, float* gram, int32_t parts, int32_t first,
                   float scale, float eps, void* p, hipStream_t stream) {
   if (dtype != QKVNR_BF16 && dtype != QKVNR_FP32) return fail(QKVNR_EINVAL, "unknown dtype %d", dtype);
-  if (blocks < 0 || blocks > INT32_MAX) return fail(QKVNR_EINVAL, "blocks %lld out of [0, 2^31)", (long long)blocks);
+  if (blocks < 0 || blocks > kMaxLaunchBlocks)  // one launch, one workgroup (row) per block
+    return fail(QKVNR_EINVAL, "blocks %lld out of [0, 2^22]", (long long)blocks);
   if (d < 1 || d > kNsMaxD) return fail(QKVNR_EUNSUPPORTED, "block side %d: the kernel holds 1..%d", d, kNsMaxD);
   if (parts < 1) return fail(QKVNR_EINVAL, "parts %d must be >= 1", parts);
   if (!std::isfinite(scale) || scale <= 0.0f) return fail(QKVNR_EINVAL, "scale %g must be finite and > 0", (double)scale);
@@ -583,7 +606,8 @@ int qkvnr_ns_poly(int32_t dtype, int64_t blocks, int32_t d, float* gram, int32_t
 
 int qkvnr_ns_update(int64_t blocks, int32_t d, int64_t cols, const void* p, const void* x, void* y,
                     int32_t parts, float* gram, hipStream_t stream) {
-  if (blocks < 0 || blocks > INT32_MAX) return fail(QKVNR_EINVAL, "blocks %lld out of [0, 2^31)", (long long)blocks);
+  if (blocks < 0 || blocks > kMaxLaunchBlocks)  // one launch, one workgroup (row) per block
+    return fail(QKVNR_EINVAL, "blocks %lld out of [0, 2^22]", (long long)blocks);
   if (d != 64 && d != 128) return fail(QKVNR_EUNSUPPORTED, "block side %d: the update kernel exists for 64 and 128", d);
   if (cols < 1 || cols % 8) return fail(QKVNR_EALIGN, "cols %lld must be a positive multiple of 8", (long long)cols);
   if (cols > (1 << 30)) return fail(QKVNR_EINVAL, "cols %lld above 2^30", (long long)cols);

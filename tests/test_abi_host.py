@@ -258,6 +258,7 @@ def test_ns_poly_argument_checks():
 
     assert call(i0=9) == qk.EINVAL
     assert call(i1=-1) == qk.EINVAL
+    assert call(i1=(1 << 22) + 1) == qk.EINVAL   # more blocks than one launch holds
     assert call(i2=129) == qk.EUNSUPPORTED
     assert call(i2=0) == qk.EUNSUPPORTED
     assert call(i4=0) == qk.EINVAL               # parts
@@ -289,6 +290,7 @@ def test_gram_partials_argument_checks():
     assert call(i4=0) == qk.EINVAL
     assert call(i2=(1 << 30) + 8) == qk.EINVAL
     assert call(i0=1 << 31) == qk.EINVAL
+    assert call(i0=(1 << 22) + 1) == qk.EINVAL   # more blocks than one launch holds
     assert call(i3=A + 8) == qk.EALIGN
     assert call(i5=B + 2) == qk.EALIGN
     assert call(i5=A + 4096) == qk.EINVAL         # out overlaps x
@@ -309,6 +311,7 @@ def test_ns_update_argument_checks():
 
     assert call(i0=-1) == qk.EINVAL
     assert call(i0=1 << 31) == qk.EINVAL
+    assert call(i0=(1 << 22) + 1) == qk.EINVAL   # more blocks than one launch holds
     assert call(i1=96) == qk.EUNSUPPORTED
     assert call(i1=32) == qk.EUNSUPPORTED
     assert call(i2=4100) == qk.EALIGN            # cols not a multiple of 8

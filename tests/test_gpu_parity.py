@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import qkv_split_head_amd as qk
-from qkv_inputs import (custom_gqa, decode_interleaved, gqa_paged, latent_paged, prefill_interleaved,
+from qkv_inputs import (custom_gqa, decode_interleaved, gqa_paged, latent_paged, prefill_interleaved, token_positions,
                         tiny_interleaved, train_sectioned)
 from tests.helpers import (announce, assert_bits_equal, assert_close, assert_values_close, gpu_available,
                            host_value, to_dev, to_host_bits)
@@ -552,6 +552,67 @@ def test_qwen3_train_16k_fwd_bwd():
     # dv lands in every token's v slots unchanged
     _, _, gv = oracle.split(dqkv, "sectioned", 8, 4, 128)
     assert_bits_equal(gv, w.dv, "train dv slots (all tokens)")
+
+
+
+def test_batches_past_one_launch():
+    """2^24 + 2^23 tokens of 3 heads (D = 64): the forward, the backward and the in-place RoPE each take two
+    launches (a dispatch holds fewer than 2^32 work-items; pieces of 2^24 work units or tokens). Sampled rows on
+    both sides of the piece boundary match the oracle, and the weight grads of the whole batch equal the sums of
+    its two halves taken in one launch each, so a piece dropped or run twice would show."""
+    T, P, h = (1 << 24) + (1 << 23), 4096, 1 << 24
+    w = custom_gqa("sectioned", "bf16", P, 1, 1, 64, seed=41, positions="random", grads=True)
+    pos_h = token_positions(T, seed=42)
+
+    def tiled(bits, row_shape):  # the P drawn rows repeated over the batch, on the device
+        return to_dev(bits, "bf16").reshape(P, -1).repeat(T // P, 1).reshape((T,) + row_shape)
+
+    qkv, pos = tiled(w.qkv, (192,)), to_dev(pos_h, "int32")
+    wq, wk = to_dev(w.q_norm_w, "bf16"), to_dev(w.k_norm_w, "bf16")
+    kw = dict(kind="sectioned", n_kv=1, q_per_kv=1, head_dim=64, eps=w.eps, theta=w.theta)
+    rng = np.random.Generator(np.random.PCG64(43))
+    toks = np.unique(np.concatenate([np.arange(3), np.arange(h - 3, h + 3), np.arange(T - 3, T),
+                                     rng.choice(T, size=40, replace=False)]))
+    sel = torch.from_numpy(toks).cuda()
+    rows = w.qkv[toks % P]
+
+    q, k, v = qk.forward(qkv, pos, wq, wk, **kw)
+    got = [to_host_bits(t.index_select(0, sel)) for t in (q, k, v)]
+    del q, k, v
+    q64, k64, vbits = oracle.forward_gqa(rows, "bf16", "sectioned", 1, 1, 64, pos_h[toks], w.q_norm_w,
+                                         w.k_norm_w, w.eps, w.theta)
+    assert_close(got[0], q64, "bf16", "q past one launch")
+    assert_close(got[1], k64, "bf16", "k past one launch")
+    assert_bits_equal(got[2], vbits, "v past one launch")
+
+    dq, dk, dv = tiled(w.dq, (1, 64)), tiled(w.dk, (1, 64)), tiled(w.dv, (1, 64))
+    dqkv, dwq, dwk = qk.backward(qkv, pos, wq, wk, dq, dk, dv, **kw)
+    got = to_host_bits(dqkv.index_select(0, sel))
+    del dqkv
+    ref = oracle.backward_gqa(rows, "bf16", "sectioned", 1, 1, 64, pos_h[toks], w.q_norm_w, w.k_norm_w,
+                              w.eps, w.theta, w.dq[toks % P], w.dk[toks % P], w.dv[toks % P])
+    gq, gk, gv = oracle.split(got, "sectioned", 1, 1, 64)
+    assert_close(gq, ref["dx_q"], "bf16", "dq slots past one launch")
+    assert_close(gk, ref["dx_k"], "bf16", "dk slots past one launch")
+    assert_bits_equal(gv, w.dv[toks % P], "dv slots past one launch")
+    halves = []
+    for a, b in ((0, h), (h, T)):
+        _, hq, hk = qk.backward(qkv[a:b], pos[a:b], wq, wk, dq[a:b], dk[a:b], dv[a:b], **kw)
+        halves.append((hq.cpu().numpy().astype(np.float64), hk.cpu().numpy().astype(np.float64)))
+    for i, (full, name) in enumerate(((dwq, "dq_norm_w"), (dwk, "dk_norm_w"))):
+        full = full.cpu().numpy().astype(np.float64)
+        a, b = halves[0][i], halves[1][i]
+        err = np.linalg.norm(full - (a + b))
+        assert err <= 1e-3 * (np.linalg.norm(a) + np.linalg.norm(b)), f"{name}: whole batch vs halves {err}"
+    del qkv, dq, dk, dv
+
+    x = tiled(w.qkv[:, :64], (1, 64))   # one head of 64 values per token, rotated in place
+    qk.rope_inplace(x, pos, rope_offset=0, rope_dim=64, theta=1e4)
+    got = to_host_bits(x.index_select(0, sel))
+    ref = oracle.rope_rotate_half(oracle.to_f64(w.qkv[toks % P, :64][:, None, :], "bf16"),
+                                  oracle.rope_angles(pos_h[toks], 1e4, 64))
+    assert_close(got, ref, "bf16", "rope in place past one launch")
+    torch.cuda.synchronize()
 
 
 # ------------------------------------------------------------------ HIP graphs
