@@ -48,6 +48,9 @@
  *     gradients, whose pointers must then be valid.
  *   - Calls on one stream are ordered; calls that overlap on different streams
  *     and write the same memory race, as for any kernel.
+ *   - A large batch may be enqueued as several launches of the same kernel
+ *     (a dispatch holds fewer than 2^32 work-items); the results do not
+ *     depend on it.
  */
 #ifndef QKVNR_H
 #define QKVNR_H
