@@ -161,8 +161,10 @@ int qkvnr_forward(const qkvnr_layout* layout, const void* qkv, const int32_t* po
  *              all zero again, so one zero-filled buffer serves any number of
  *              calls in sequence.  Calls that may run at the same time (on
  *              different streams) need different workspaces.  After a call
- *              that did not complete (a device fault), zero it again.  It may
- *              be NULL when T == 0.
+ *              that returned QKVNR_EHIP (a launch failed once kernels were
+ *              enqueued; the library still enqueues the fold that zeroes the
+ *              slots, but that launch may have failed too) or did not complete
+ *              (a device fault), zero it again.  It may be NULL when T == 0.
  * LATENT is QKVNR_EUNSUPPORTED.
  */
 int qkvnr_backward(const qkvnr_layout* layout, const void* qkv, const int32_t* positions,

@@ -207,6 +207,21 @@ def backward_workspace(device=None) -> torch.Tensor:
     return ws
 
 
+def _keep_workspace_clean(call, ws, device_index) -> None:
+    """Runs a backward call on workspace ``ws``.  A call that fails with QKVNR_EHIP
+    may have enqueued kernels whose partial sums stay in the workspace (the
+    library still enqueues the fold that zeroes them, but that launch may have
+    failed too), so this module's cached workspace of that device is dropped and
+    the next call allocates a zero-filled one.  Validation errors enqueue nothing
+    and keep it."""
+    try:
+        call()
+    except QkvnrError as e:
+        if e.code == EHIP and _workspaces.get(device_index) is ws:
+            del _workspaces[device_index]
+        raise
+
+
 def qkvnr_forward_paged(layout: Layout, qkv, positions, q_norm_w, k_norm_w, eps: float, theta: float,
                         block_table, bt_stride: int, tokens_per_req: int, page_size: int, num_pages: int,
                         q, k_pool, v_pool, stream=None) -> None:
@@ -334,8 +349,10 @@ def backward(qkv: torch.Tensor, positions: Optional[torch.Tensor], q_norm_w: tor
         _need(dwk, "dk_norm_w", device=qkv.device, dtype=torch.float32, shape=(head_dim,))
     ws = backward_workspace(qkv.device) if workspace is None else workspace
     _need(ws, "workspace", device=qkv.device)
-    qkvnr_backward(L, qkv, positions, q_norm_w, k_norm_w, eps, theta, dq, dk, dv, dqkv, dwq, dwk, ws,
-                   ws.numel() * ws.element_size(), stream)
+    _keep_workspace_clean(
+        lambda: qkvnr_backward(L, qkv, positions, q_norm_w, k_norm_w, eps, theta, dq, dk, dv, dqkv, dwq, dwk, ws,
+                               ws.numel() * ws.element_size(), stream),
+        ws, qkv.device.index)
     return dqkv, dwq, dwk
 
 

@@ -40,7 +40,8 @@ DeviceInfo g_devices[kMaxDevices];
 std::mutex g_devices_mu;
 
 // Compute units of the current device, or an error if it is not a gfx950.
-int current_device(int* cus) {
+// `index`, when given, receives the device's index.
+int current_device(int* cus, int* index = nullptr) {
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(QKVNR_EUNSUPPORTED, "no HIP device is current: %s", hipGetErrorString(e));
@@ -57,6 +58,7 @@ int current_device(int* cus) {
   }
   if (!d.gfx950) return fail(QKVNR_EUNSUPPORTED, "device %d is not gfx950; this library has kernels for gfx950 only", dev);
   *cus = d.cus;
+  if (index) *index = dev;
   return QKVNR_OK;
 }
 
@@ -224,14 +226,16 @@ constexpr int64_t kMaxLaunchBlocks = int64_t(1) << 22;
 
 // Launches launch(grid) once per piece of at most kMaxLaunchBlocks blocks over `items` work
 // items of `per_block` per block, after set_first(first item of the piece); stops at the first
-// launch that fails.
+// launch that fails.  `enqueued`, when given, is set if at least one piece went out.
 template <typename SetFirst, typename Launch>
-int launch_pieces(int64_t items, int per_block, const char* what, SetFirst&& set_first, Launch&& launch) {
+int launch_pieces(int64_t items, int per_block, const char* what, SetFirst&& set_first, Launch&& launch,
+                  bool* enqueued = nullptr) {
   const int64_t blocks = (items + per_block - 1) / per_block;
   for (int64_t b0 = 0; b0 < blocks; b0 += kMaxLaunchBlocks) {
     set_first(b0 * per_block);
     launch(dim3(static_cast<uint32_t>(std::min(kMaxLaunchBlocks, blocks - b0))));
     if (int rc = launched(what)) return rc;
+    if (enqueued) *enqueued = true;
   }
   return QKVNR_OK;
 }
@@ -258,7 +262,7 @@ int launch_fwd_gqa(GqaArgs a, int32_t dtype, int32_t D, bool rope, hipStream_t s
   return launch_pieces(a.units, kWavesPerBlock, "forward", [&](int64_t u0) { a.unit0 = u0; }, launch);
 }
 
-int launch_bwd_gqa(GqaArgs a, int32_t dtype, int32_t D, bool rope, hipStream_t s) {
+int launch_bwd_gqa(GqaArgs a, int32_t dtype, int32_t D, bool rope, hipStream_t s, bool* enqueued) {
   const dim3 b(kBwdBlockThreads);
   auto launch = [&](dim3 g) {
 #define QKVNR_BWD(IO, DD, R) hipLaunchKernelGGL((bwd_gqa_kernel<IO, DD, R>), g, b, QKVNR_BWD_LDS, s, a)
@@ -271,7 +275,8 @@ int launch_bwd_gqa(GqaArgs a, int32_t dtype, int32_t D, bool rope, hipStream_t s
     }
 #undef QKVNR_BWD
   };
-  return launch_pieces(a.units, kBwdWavesPerBlock, "backward", [&](int64_t u0) { a.unit0 = u0; }, launch);
+  return launch_pieces(a.units, kBwdWavesPerBlock, "backward", [&](int64_t u0) { a.unit0 = u0; }, launch,
+                       enqueued);
 }
 
 constexpr int kLatentBlocksPerCu = 8;
@@ -363,6 +368,81 @@ int gqa_forward(const qkvnr_layout* L, const void* qkv, const int32_t* positions
   return launch_fwd_gqa<false, kFwdU, kFwdDepth>(a, L->dtype, L->head_dim, rope, stream);
 }
 
+// ------------------------------------------------------------------ backward
+
+// The backward and its weight-grad fold.
+int backward_impl(const qkvnr_layout* layout, const void* qkv, const int32_t* positions, const void* q_norm_w,
+                  const void* k_norm_w, float eps, double theta, const void* dq, const void* dk, const void* dv,
+                  void* dqkv, float* dq_norm_w, float* dk_norm_w, void* workspace, int64_t workspace_bytes,
+                  hipStream_t stream) {
+  if (int rc = check_layout(layout)) return rc;
+  const qkvnr_layout* L = layout;
+  if (L->kind == QKVNR_LATENT) return fail(QKVNR_EUNSUPPORTED, "backward of latent rows has no kernel");
+  if (int rc = check_scalars(L, eps, theta)) return rc;
+  const bool rope = L->rope_dim > 0;
+  const int es = elem_bytes(L->dtype);
+  if (int rc = need4(dq_norm_w, "dq_norm_w")) return rc;
+  if (int rc = need4(dk_norm_w, "dk_norm_w")) return rc;
+  const int64_t D = L->head_dim, n_q = static_cast<int64_t>(L->n_kv) * L->q_per_kv;
+  if (overlaps({dq_norm_w, D * 4}, {dk_norm_w, D * 4})) return fail(QKVNR_EINVAL, "two outputs overlap");
+  const int64_t ws_need = static_cast<int64_t>(kWgradSlots) * 2 * D * static_cast<int64_t>(sizeof(float));
+  int cus = 0;
+  if (L->T == 0) {  // no token is read and the slots are not touched: the weight grads are zero
+    if (int rc = current_device(&cus)) return rc;
+    hipLaunchKernelGGL(zero2_f32_kernel, dim3(1), dim3(256), 0, stream, dq_norm_w, dk_norm_w, static_cast<int>(D));
+    return launched("weight-grad zeroing");
+  }
+  if (int rc = need16(qkv, "qkv")) return rc;
+  if (rope) {
+    if (int rc = need4(positions, "positions")) return rc;
+  }
+  if (int rc = need16(q_norm_w, "q_norm_w")) return rc;
+  if (int rc = need16(k_norm_w, "k_norm_w")) return rc;
+  if (int rc = need16(dq, "dq")) return rc;
+  if (int rc = need16(dk, "dk")) return rc;
+  if (int rc = need16(dv, "dv")) return rc;
+  if (int rc = need16(dqkv, "dqkv")) return rc;
+  if (int rc = need16(workspace, "workspace")) return rc;
+  if (workspace_bytes < ws_need)
+    return fail(QKVNR_EINVAL, "workspace of %lld bytes is smaller than the %lld needed", (long long)workspace_bytes,
+                (long long)ws_need);
+  const int64_t kvb = L->T * L->n_kv * D * es;
+  if (int rc = check_disjoint(
+          {{dqkv, rows_extent(L, es)}, {dq_norm_w, D * 4}, {dk_norm_w, D * 4}, {workspace, ws_need}},
+          {{qkv, rows_extent(L, es)}, {positions, positions ? L->T * 4 : 0}, {q_norm_w, D * es},
+           {k_norm_w, D * es}, {dq, L->T * n_q * D * es}, {dk, kvb}, {dv, kvb}}))
+    return rc;
+  if (int rc = current_device(&cus)) return rc;
+  GqaArgs a{};
+  plan_gqa(a, L, kBwdU, theta);
+  a.qkv = static_cast<const uint8_t*>(qkv);
+  a.pos = positions;
+  a.wq = static_cast<const uint8_t*>(q_norm_w);
+  a.wk = static_cast<const uint8_t*>(k_norm_w);
+  a.dq = static_cast<const uint8_t*>(dq);
+  a.dk = static_cast<const uint8_t*>(dk);
+  a.dv = static_cast<const uint8_t*>(dv);
+  a.dqkv = static_cast<uint8_t*>(dqkv);
+  a.dwq = dq_norm_w;
+  a.dwk = dk_norm_w;
+  a.slots = static_cast<float*>(workspace);
+  a.eps = eps;
+  bool enqueued = false;
+  const int rc_bwd = launch_bwd_gqa(a, L->dtype, L->head_dim, rope, stream, &enqueued);
+  if (!enqueued) return rc_bwd;  // nothing reached the slots
+  // Once any piece is enqueued its atomics reach the slots, so the fold, which
+  // zeroes them again, is enqueued even when a later piece failed to launch.
+  if (D == 64)
+    hipLaunchKernelGGL(wgrad_fold_kernel<64>, dim3(1), dim3(kFoldThreads), 0, stream, a.slots, dq_norm_w, dk_norm_w);
+  else
+    hipLaunchKernelGGL(wgrad_fold_kernel<128>, dim3(1), dim3(kFoldThreads), 0, stream, a.slots, dq_norm_w, dk_norm_w);
+  const hipError_t fold_err = hipGetLastError();
+  if (fold_err == hipSuccess) return rc_bwd;
+  // the slots keep this call's partial sums: the caller must zero the workspace again
+  if (rc_bwd != QKVNR_OK) return rc_bwd;  // keep the first failure's message
+  return fail(QKVNR_EHIP, "weight-grad fold launch failed: %s", hipGetErrorString(fold_err));
+}
+
 template <int D, bool ROPE>
 void launch_proj(const ProjArgs& a, bool tail, dim3 grid, dim3 block, hipStream_t stream) {
   if (tail) hipLaunchKernelGGL((proj_qkv_kernel<D, ROPE, true>), grid, block, 0, stream, a);
@@ -420,64 +500,8 @@ int qkvnr_backward(const qkvnr_layout* layout, const void* qkv, const int32_t* p
                    const void* k_norm_w, float eps, double theta, const void* dq, const void* dk, const void* dv,
                    void* dqkv, float* dq_norm_w, float* dk_norm_w, void* workspace, int64_t workspace_bytes,
                    hipStream_t stream) {
-  if (int rc = check_layout(layout)) return rc;
-  const qkvnr_layout* L = layout;
-  if (L->kind == QKVNR_LATENT) return fail(QKVNR_EUNSUPPORTED, "backward of latent rows has no kernel");
-  if (int rc = check_scalars(L, eps, theta)) return rc;
-  const bool rope = L->rope_dim > 0;
-  const int es = elem_bytes(L->dtype);
-  if (int rc = need4(dq_norm_w, "dq_norm_w")) return rc;
-  if (int rc = need4(dk_norm_w, "dk_norm_w")) return rc;
-  const int64_t D = L->head_dim, n_q = static_cast<int64_t>(L->n_kv) * L->q_per_kv;
-  if (overlaps({dq_norm_w, D * 4}, {dk_norm_w, D * 4})) return fail(QKVNR_EINVAL, "two outputs overlap");
-  int cus = 0;
-  if (L->T == 0) {  // no token is read and the workspace is not touched: the weight grads are zero
-    if (int rc = current_device(&cus)) return rc;
-    hipLaunchKernelGGL(zero2_f32_kernel, dim3(1), dim3(256), 0, stream, dq_norm_w, dk_norm_w, static_cast<int>(D));
-    return launched("weight-grad zeroing");
-  }
-  if (int rc = need16(qkv, "qkv")) return rc;
-  if (rope) {
-    if (int rc = need4(positions, "positions")) return rc;
-  }
-  if (int rc = need16(q_norm_w, "q_norm_w")) return rc;
-  if (int rc = need16(k_norm_w, "k_norm_w")) return rc;
-  if (int rc = need16(dq, "dq")) return rc;
-  if (int rc = need16(dk, "dk")) return rc;
-  if (int rc = need16(dv, "dv")) return rc;
-  if (int rc = need16(dqkv, "dqkv")) return rc;
-  if (int rc = need16(workspace, "workspace")) return rc;
-  const int64_t ws_need = qkvnr_backward_workspace_bytes(L);
-  if (workspace_bytes < ws_need)
-    return fail(QKVNR_EINVAL, "workspace of %lld bytes is smaller than the %lld needed", (long long)workspace_bytes,
-                (long long)ws_need);
-  const int64_t kvb = L->T * L->n_kv * D * es;
-  if (int rc = check_disjoint(
-          {{dqkv, rows_extent(L, es)}, {dq_norm_w, D * 4}, {dk_norm_w, D * 4}, {workspace, ws_need}},
-          {{qkv, rows_extent(L, es)}, {positions, positions ? L->T * 4 : 0}, {q_norm_w, D * es},
-           {k_norm_w, D * es}, {dq, L->T * n_q * D * es}, {dk, kvb}, {dv, kvb}}))
-    return rc;
-  if (int rc = current_device(&cus)) return rc;
-  GqaArgs a{};
-  plan_gqa(a, L, kBwdU, theta);
-  a.qkv = static_cast<const uint8_t*>(qkv);
-  a.pos = positions;
-  a.wq = static_cast<const uint8_t*>(q_norm_w);
-  a.wk = static_cast<const uint8_t*>(k_norm_w);
-  a.dq = static_cast<const uint8_t*>(dq);
-  a.dk = static_cast<const uint8_t*>(dk);
-  a.dv = static_cast<const uint8_t*>(dv);
-  a.dqkv = static_cast<uint8_t*>(dqkv);
-  a.dwq = dq_norm_w;
-  a.dwk = dk_norm_w;
-  a.slots = static_cast<float*>(workspace);
-  a.eps = eps;
-  if (int rc = launch_bwd_gqa(a, L->dtype, L->head_dim, rope, stream)) return rc;
-  if (D == 64)
-    hipLaunchKernelGGL(wgrad_fold_kernel<64>, dim3(1), dim3(kFoldThreads), 0, stream, a.slots, dq_norm_w, dk_norm_w);
-  else
-    hipLaunchKernelGGL(wgrad_fold_kernel<128>, dim3(1), dim3(kFoldThreads), 0, stream, a.slots, dq_norm_w, dk_norm_w);
-  return launched("weight-grad fold");
+  return backward_impl(layout, qkv, positions, q_norm_w, k_norm_w, eps, theta, dq, dk, dv, dqkv, dq_norm_w,
+                       dk_norm_w, workspace, workspace_bytes, stream);
 }
 
 int qkvnr_rope_inplace(int32_t dtype, int64_t T, int32_t heads, int64_t token_stride, int32_t head_stride,

@@ -193,7 +193,7 @@ class MlaDrafterLayer:
         if pool.shape[-1] != d.kv_lora_rank + d.qk_rope_head_dim:
             raise ValueError("pool rows must hold kv_lora_rank + rope values")
         if not direct_pool_write and slots is None and not torch.cuda.is_current_stream_capturing():
-            _, ok = pool_slots(positions, block_table, tokens_per_req, pool.shape[1])
+            _, ok = pool_slots(positions, block_table, tokens_per_req, pool.shape[1], pool.shape[0])
             if not bool(ok.all()):
                 raise ValueError("the staged pool write needs every token mapped by the block table")
         xn = self.input_norm(x)
@@ -233,19 +233,22 @@ def staged_slots(positions: torch.Tensor, block_table: torch.Tensor, tokens_per_
                  num_slots: int) -> torch.Tensor:
     """Flat pool slots for the staged write (every token must be mapped; see :func:`pool_slots`),
     clamped into [0, num_slots) so that the scatter stays in bounds whatever the table holds."""
-    slot, _ = pool_slots(positions, block_table, tokens_per_req, page_size)
+    slot, _ = pool_slots(positions, block_table, tokens_per_req, page_size, num_slots // page_size)
     return slot.clamp(0, num_slots - 1)
 
 
 def pool_slots(positions: torch.Tensor, block_table: torch.Tensor, tokens_per_req: int,
-               page_size: int) -> Tuple[torch.Tensor, torch.Tensor]:
+               page_size: int, num_pages: int) -> Tuple[torch.Tensor, torch.Tensor]:
     """Flat pool slot of each token and whether the table maps it (for the staged write,
-    whose scatter needs every token mapped, as a drafter's tokens always are)."""
+    whose scatter needs every token mapped, as a drafter's tokens always are).  A token is
+    mapped when its position is >= 0, its page index is inside the table's row and the
+    page id is in [0, num_pages): the rule of the direct pool write, which skips any other
+    token."""
     N = positions.shape[0]
     pos = positions.to(torch.int64)
     req = torch.arange(N, device=positions.device) // tokens_per_req
     pi = pos // page_size
     ok = (pos >= 0) & (pi < block_table.shape[1])
     page = block_table[req, pi.clamp(0, block_table.shape[1] - 1)].to(torch.int64)
-    ok = ok & (page >= 0)
+    ok = ok & (page >= 0) & (page < num_pages)
     return page * page_size + pos % page_size, ok
