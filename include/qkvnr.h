@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define QKVNR_VERSION 10301 /* major * 10000 + minor * 100 + patch */
+#define QKVNR_VERSION 10400 /* major * 10000 + minor * 100 + patch */
 
 /* Return codes. */
 #define QKVNR_OK 0
@@ -177,6 +177,32 @@ int qkvnr_backward(const qkvnr_layout* layout, const void* qkv, const int32_t* p
  * QKVNR_BACKWARD_WORKSPACE_MAX for any supported layout). */
 int64_t qkvnr_backward_workspace_bytes(const qkvnr_layout* layout);
 #define QKVNR_BACKWARD_WORKSPACE_MAX 16384
+
+/*
+ * qkvnr_backward without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, serving loops that may
+ * not call hipMalloc, harnesses that forbid allocation.  Same arguments (less
+ * workspace and workspace_bytes), arithmetic, results and errors as
+ * qkvnr_backward.  The weight-grad partial-sum slots live in a static device
+ * array inside the library, QKVNR_NOALLOC_SCRATCH_BYTES bytes, one copy per GPU,
+ * held until the process ends.  No hipMalloc, hipFree or allocating call is
+ * made.
+ *   - The first call on a device looks the array up (hipGetSymbolAddress) and
+ *     enqueues, on `stream`, a small kernel that zeroes it.  Every completed
+ *     call leaves it zero; a call whose fold failed to launch (QKVNR_EHIP)
+ *     makes the next call on that device zero it again first.
+ *   - Every call on one GPU shares that GPU's array: calls that may overlap in
+ *     time on one GPU (different streams, no ordering between them) race, and
+ *     their weight grads are wrong.  Order such calls, or give each stream
+ *     its own workspace through qkvnr_backward.
+ *   - A layout whose slots (qkvnr_backward_workspace_bytes) exceed the array
+ *     is QKVNR_EINVAL; every supported head_dim fits.
+ */
+int qkvnr_backward_noalloc(const qkvnr_layout* layout, const void* qkv, const int32_t* positions,
+                           const void* q_norm_w, const void* k_norm_w, float eps, double theta,
+                           const void* dq, const void* dk, const void* dv, void* dqkv,
+                           float* dq_norm_w, float* dk_norm_w, hipStream_t stream);
+#define QKVNR_NOALLOC_SCRATCH_BYTES 16384
 
 /*
  * Forward that stores k and v (GQA kinds) or the latent row (LATENT) straight

@@ -35,6 +35,7 @@ from ._binding import (  # noqa: F401
     lib,
     proj_forward,
     qkvnr_backward,
+    qkvnr_backward_noalloc,
     qkvnr_backward_workspace_bytes,
     qkvnr_forward,
     qkvnr_forward_paged,

@@ -69,6 +69,9 @@ def lib() -> ctypes.CDLL:
         L.qkvnr_backward.argtypes = [lp, vp, i32p, vp, vp, ctypes.c_float, ctypes.c_double, vp, vp, vp, vp,
                                      f32p, f32p, vp, ctypes.c_int64, vp]
         L.qkvnr_backward.restype = ctypes.c_int
+        L.qkvnr_backward_noalloc.argtypes = [lp, vp, i32p, vp, vp, ctypes.c_float, ctypes.c_double, vp, vp, vp,
+                                             vp, f32p, f32p, vp]
+        L.qkvnr_backward_noalloc.restype = ctypes.c_int
         L.qkvnr_backward_workspace_bytes.argtypes = [lp]
         L.qkvnr_backward_workspace_bytes.restype = ctypes.c_int64
         L.qkvnr_forward_paged.argtypes = [lp, vp, i32p, vp, vp, ctypes.c_float, ctypes.c_double, i32p,
@@ -178,6 +181,14 @@ def qkvnr_backward(layout: Layout, qkv, positions, q_norm_w, k_norm_w, eps: floa
     _check(lib().qkvnr_backward(ctypes.byref(layout), _ptr(qkv), _ptr(positions), _ptr(q_norm_w), _ptr(k_norm_w),
                                 eps, theta, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dqkv), _ptr(dq_norm_w),
                                 _ptr(dk_norm_w), _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def qkvnr_backward_noalloc(layout: Layout, qkv, positions, q_norm_w, k_norm_w, eps: float, theta: float, dq, dk,
+                           dv, dqkv, dq_norm_w, dk_norm_w, stream=None) -> None:
+    """Call ``qkvnr_backward_noalloc`` (the weight-grad slots live inside the library)."""
+    _check(lib().qkvnr_backward_noalloc(ctypes.byref(layout), _ptr(qkv), _ptr(positions), _ptr(q_norm_w),
+                                        _ptr(k_norm_w), eps, theta, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dqkv),
+                                        _ptr(dq_norm_w), _ptr(dk_norm_w), _stream(stream)))
 
 
 def qkvnr_backward_workspace_bytes(layout: Layout) -> int:

@@ -14,6 +14,13 @@
 #include "proj.h"
 #include "qkvnr.h"
 
+// The weight-grad slots of qkvnr_backward_noalloc: the library's own device
+// memory, one copy per GPU (each device that loads the library holds it until
+// the process ends).  In host code `scratch` is only a stand-in for the
+// symbol, not a device address: kernels get the address that
+// hipGetSymbolAddress returns for the current device (library_scratch below).
+static __device__ __align__(256) uint8_t scratch[QKVNR_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 using namespace qkvnr;
@@ -370,11 +377,54 @@ int gqa_forward(const qkvnr_layout* L, const void* qkv, const int32_t* positions
 
 // ------------------------------------------------------------------ backward
 
-// The backward and its weight-grad fold.
+static_assert(static_cast<int64_t>(kWgradSlots) * 2 * 128 * sizeof(float) <= QKVNR_NOALLOC_SCRATCH_BYTES,
+              "the library's scratch holds the slots of the widest head");
+
+struct ScratchState {
+  void* ptr = nullptr;  // device address of `scratch` on this device
+  bool dirty = true;    // zero it before the next use (first use, or a call whose fold failed to launch)
+};
+ScratchState g_scratch[kMaxDevices];  // guarded by g_scratch_mu
+std::mutex g_scratch_mu;
+
+__global__ void zero_u32_kernel(uint32_t* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+// The device address of this device's scratch, looked up on its first use, and
+// zeroed on `stream` (a kernel, so that a caller may capture it) when it may
+// hold anything but zeros.
+int library_scratch(int dev, hipStream_t stream, void** out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ScratchState& st = g_scratch[dev];
+  if (!st.ptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(QKVNR_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    st.ptr = p;
+  }
+  if (st.dirty) {
+    hipLaunchKernelGGL(zero_u32_kernel, dim3(4), dim3(1024), 0, stream, static_cast<uint32_t*>(st.ptr),
+                       QKVNR_NOALLOC_SCRATCH_BYTES / 4);
+    if (int rc = launched("scratch zeroing")) return rc;
+    st.dirty = false;
+  }
+  *out = st.ptr;
+  return QKVNR_OK;
+}
+
+void mark_scratch_dirty(int dev) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  g_scratch[dev].dirty = true;
+}
+
+// qkvnr_backward (caller's workspace) and qkvnr_backward_noalloc (the library's
+// scratch, when use_scratch) share everything but where the slots live.
 int backward_impl(const qkvnr_layout* layout, const void* qkv, const int32_t* positions, const void* q_norm_w,
                   const void* k_norm_w, float eps, double theta, const void* dq, const void* dk, const void* dv,
                   void* dqkv, float* dq_norm_w, float* dk_norm_w, void* workspace, int64_t workspace_bytes,
-                  hipStream_t stream) {
+                  bool use_scratch, hipStream_t stream) {
   if (int rc = check_layout(layout)) return rc;
   const qkvnr_layout* L = layout;
   if (L->kind == QKVNR_LATENT) return fail(QKVNR_EUNSUPPORTED, "backward of latent rows has no kernel");
@@ -386,7 +436,10 @@ int backward_impl(const qkvnr_layout* layout, const void* qkv, const int32_t* po
   const int64_t D = L->head_dim, n_q = static_cast<int64_t>(L->n_kv) * L->q_per_kv;
   if (overlaps({dq_norm_w, D * 4}, {dk_norm_w, D * 4})) return fail(QKVNR_EINVAL, "two outputs overlap");
   const int64_t ws_need = static_cast<int64_t>(kWgradSlots) * 2 * D * static_cast<int64_t>(sizeof(float));
-  int cus = 0;
+  if (use_scratch && ws_need > QKVNR_NOALLOC_SCRATCH_BYTES)
+    return fail(QKVNR_EINVAL, "head_dim %lld needs %lld bytes of weight-grad slots; the library's scratch holds %d",
+                (long long)D, (long long)ws_need, QKVNR_NOALLOC_SCRATCH_BYTES);
+  int cus = 0, dev = -1;
   if (L->T == 0) {  // no token is read and the slots are not touched: the weight grads are zero
     if (int rc = current_device(&cus)) return rc;
     hipLaunchKernelGGL(zero2_f32_kernel, dim3(1), dim3(256), 0, stream, dq_norm_w, dk_norm_w, static_cast<int>(D));
@@ -402,17 +455,22 @@ int backward_impl(const qkvnr_layout* layout, const void* qkv, const int32_t* po
   if (int rc = need16(dk, "dk")) return rc;
   if (int rc = need16(dv, "dv")) return rc;
   if (int rc = need16(dqkv, "dqkv")) return rc;
-  if (int rc = need16(workspace, "workspace")) return rc;
-  if (workspace_bytes < ws_need)
-    return fail(QKVNR_EINVAL, "workspace of %lld bytes is smaller than the %lld needed", (long long)workspace_bytes,
-                (long long)ws_need);
+  if (!use_scratch) {
+    if (int rc = need16(workspace, "workspace")) return rc;
+    if (workspace_bytes < ws_need)
+      return fail(QKVNR_EINVAL, "workspace of %lld bytes is smaller than the %lld needed", (long long)workspace_bytes,
+                  (long long)ws_need);
+  }
   const int64_t kvb = L->T * L->n_kv * D * es;
   if (int rc = check_disjoint(
-          {{dqkv, rows_extent(L, es)}, {dq_norm_w, D * 4}, {dk_norm_w, D * 4}, {workspace, ws_need}},
+          {{dqkv, rows_extent(L, es)}, {dq_norm_w, D * 4}, {dk_norm_w, D * 4}, {workspace, use_scratch ? 0 : ws_need}},
           {{qkv, rows_extent(L, es)}, {positions, positions ? L->T * 4 : 0}, {q_norm_w, D * es},
            {k_norm_w, D * es}, {dq, L->T * n_q * D * es}, {dk, kvb}, {dv, kvb}}))
     return rc;
-  if (int rc = current_device(&cus)) return rc;
+  if (int rc = current_device(&cus, &dev)) return rc;
+  if (use_scratch) {
+    if (int rc = library_scratch(dev, stream, &workspace)) return rc;
+  }
   GqaArgs a{};
   plan_gqa(a, L, kBwdU, theta);
   a.qkv = static_cast<const uint8_t*>(qkv);
@@ -438,7 +496,8 @@ int backward_impl(const qkvnr_layout* layout, const void* qkv, const int32_t* po
     hipLaunchKernelGGL(wgrad_fold_kernel<128>, dim3(1), dim3(kFoldThreads), 0, stream, a.slots, dq_norm_w, dk_norm_w);
   const hipError_t fold_err = hipGetLastError();
   if (fold_err == hipSuccess) return rc_bwd;
-  // the slots keep this call's partial sums: the caller must zero the workspace again
+  // the slots keep this call's partial sums: they must be zeroed before the next use
+  if (use_scratch) mark_scratch_dirty(dev);
   if (rc_bwd != QKVNR_OK) return rc_bwd;  // keep the first failure's message
   return fail(QKVNR_EHIP, "weight-grad fold launch failed: %s", hipGetErrorString(fold_err));
 }
@@ -501,7 +560,15 @@ int qkvnr_backward(const qkvnr_layout* layout, const void* qkv, const int32_t* p
                    void* dqkv, float* dq_norm_w, float* dk_norm_w, void* workspace, int64_t workspace_bytes,
                    hipStream_t stream) {
   return backward_impl(layout, qkv, positions, q_norm_w, k_norm_w, eps, theta, dq, dk, dv, dqkv, dq_norm_w,
-                       dk_norm_w, workspace, workspace_bytes, stream);
+                       dk_norm_w, workspace, workspace_bytes, false, stream);
+}
+
+int qkvnr_backward_noalloc(const qkvnr_layout* layout, const void* qkv, const int32_t* positions,
+                           const void* q_norm_w, const void* k_norm_w, float eps, double theta, const void* dq,
+                           const void* dk, const void* dv, void* dqkv, float* dq_norm_w, float* dk_norm_w,
+                           hipStream_t stream) {
+  return backward_impl(layout, qkv, positions, q_norm_w, k_norm_w, eps, theta, dq, dk, dv, dqkv, dq_norm_w,
+                       dk_norm_w, nullptr, 0, true, stream);
 }
 
 int qkvnr_rope_inplace(int32_t dtype, int64_t T, int32_t heads, int64_t token_stride, int32_t head_stride,

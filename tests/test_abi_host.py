@@ -167,6 +167,36 @@ def test_backward_argument_checks():
     assert call(i12=A + 4096) == qk.EINVAL               # workspace overlaps qkv
 
 
+def test_backward_noalloc_argument_checks():
+    """The no-alloc backward validates like qkvnr_backward (less the workspace) before any HIP call."""
+    L = _lay()
+    f = qk.lib().qkvnr_backward_noalloc
+    args = [A, B, C, C + 4096, 1e-6, 1e4, Dp, E, F, A + (6 << 30), A + (7 << 30), A + (7 << 30) + 4096]
+
+    def call(layout=L, **change):
+        a = list(args)
+        for i, v in change.items():
+            a[int(i[1:])] = v
+        return f(ctypes.byref(layout), *a, None)
+
+    assert f(None, *args, None) == qk.EINVAL             # no layout
+    assert call(i9=0) == qk.EINVAL                       # dqkv NULL
+    assert call(i10=A + (7 << 30) + 2) == qk.EALIGN      # dq_norm_w misaligned
+    assert call(i9=A + 64) == qk.EINVAL                  # dqkv overlaps qkv
+    assert call(i11=A + (7 << 30) + 8) == qk.EINVAL      # the two weight grads overlap
+    assert call(i4=-1.0) == qk.EINVAL                    # eps
+    assert call(layout=_lay(width=100)) == qk.EINVAL     # not the exact total
+    assert call(layout=_lay(head_dim=96, width=(16 * 8 + 32) * 96, rope_dim=96)) == qk.EUNSUPPORTED
+    lat = _lay(kind=qk.LATENT, n_kv=1, q_per_kv=0, head_dim=0, rope_dim=64, width=576, norm_dim=512)
+    assert call(layout=lat) == qk.EUNSUPPORTED           # no latent backward
+
+
+def test_noalloc_scratch_size_in_header():
+    text = open(qk._binding.HEADER).read()
+    cap = int(re.search(r"#define QKVNR_NOALLOC_SCRATCH_BYTES (\d+)", text).group(1))
+    assert cap >= qk.lib().qkvnr_backward_workspace_bytes(None)
+
+
 def test_backward_workspace_size():
     L128 = _lay(n_kv=8, q_per_kv=4, head_dim=128, rope_dim=128)
     L64 = _lay()
