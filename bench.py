@@ -13,10 +13,19 @@ the backward on set (i - 1) mod 3 (a batch whose forward ran a step earlier,
 as in a model where other layers run between a layer's forward and backward),
 so no read finds data left in the cache by the previous ~0.97 GB of traffic.
 
-Also reported (``extras``): Muse-Spark decode at T = 1/8/64/256 (HIP-graph
-replays, us per call), Muse prefill at T = 16384 as a RoPE and a NoPE layer
-(us, GB/s), the MLA latent paged store (us), and the CPU oracle on a bounded
-sample of the step's workload (``cpu_baseline``).
+Clock settling: an idle GPU takes tens of milliseconds to reach its working
+clocks.  Before the counted ``--warmup`` steps, full steps run until the clocks
+have settled (at least 250 ms, then until two successive 25-step batches agree
+within 1 %, at most 3 s); the JSON line reports how long (``settle``).  The
+timed region is exactly ``--steps`` steps either way.
+
+Also reported (``extras``, legs chosen with ``--legs``): Muse-Spark decode at
+T = 1/8/64/256 (HIP-graph replays, us per call), Muse prefill at T = 16384 as a
+RoPE and a NoPE layer (us, GB/s), the MLA latent paged store (us), the MLA
+drafter layer's schedules, per-head Newton-Schulz and the fused projection.
+The CPU oracle runs first, on one host core and on all of them, on bounded
+samples of every workload (``cpu_baseline``; its us per layer also sit beside
+each GPU figure in ``extras`` as ``*_oracle_us``).
 
 Prints one JSON line.  Only one GPU: ``--gpus`` above 1 exits with a message.
 """
@@ -74,33 +83,162 @@ def traffic_from_profile():
         return None
 
 
-def cpu_baseline(target_s: float = 12.0):
-    """Oracle (NumPy fp64, single thread) on the step's workload, token chunks until ~target_s."""
-    import oracle
-    from qkv_inputs import train_sectioned
+# ---------------------------------------------------------------- CPU oracle baseline
 
-    w = train_sectioned(2048)
-    fwd_b, bwd_b = gqa_bytes(1, 32, 8, 128, 2)
-    done = 0
+# The oracle's sample of each workload: the generator's batch of the same shape
+# (the training and prefill configs: its first 2048 tokens, positions 0..2047),
+# keyed by the name its GPU figure has in ``extras``.
+_CPU_W = {}
+_CPU_CHUNK = 256
+
+
+def _cpu_workloads():
+    from qkv_inputs import decode_interleaved, latent_paged, prefill_interleaved, train_sectioned
+
+    w = {"train_fwd_plus_bwd": train_sectioned(2048),
+         "prefill_rope": prefill_interleaved(2048, rope=True),
+         "prefill_nope": prefill_interleaved(2048, rope=False)}
+    for T in (1, 8, 64, 256):
+        w[f"decode_T{T}"] = decode_interleaved(T)
+    w["mla_latent_paged_B4xT16"] = latent_paged()
+    return w
+
+
+def _oracle_gqa(name, t0, t1):
+    """The oracle's path over tokens [t0, t1) of a GQA workload: outputs rounded once to bf16
+    (forward), and for the training config also the backward's packed grad."""
+    import oracle
+
+    w = _CPU_W[name]
+    sl = slice(t0, t1)
+    rope = w.rope_dim > 0
+    q64, k64, _ = oracle.forward_gqa(w.qkv[sl], w.dtype, w.kind, w.n_kv, w.q_per_kv, w.head_dim, w.positions[sl],
+                                     w.q_norm_w, w.k_norm_w, w.eps, w.theta, rope=rope)
+    oracle.round_to_storage(q64, w.dtype)
+    oracle.round_to_storage(k64, w.dtype)
+    if w.dq is not None:
+        ref = oracle.backward_gqa(w.qkv[sl], w.dtype, w.kind, w.n_kv, w.q_per_kv, w.head_dim, w.positions[sl],
+                                  w.q_norm_w, w.k_norm_w, w.eps, w.theta, w.dq[sl], w.dk[sl], w.dv[sl], rope=rope)
+        oracle.round_to_storage(ref["dqkv64"], w.dtype)
+    return t1 - t0
+
+
+def _oracle_latent_rows(t0, t1):
+    import oracle
+
+    w = _CPU_W["mla_latent_paged_B4xT16"]
+    rows = oracle.latent_forward(w.qkv[t0:t1], "bf16", w.positions[t0:t1], w.k_norm_w, w.eps, w.theta, 512, 64)
+    return oracle.round_to_storage(rows, "bf16")
+
+
+def _oracle_latent_store(pool, rows):
+    import oracle
+
+    w = _CPU_W["mla_latent_paged_B4xT16"]
+    page, off = oracle.paged_slots(w.positions, w.block_table, w.tokens_per_req, w.page_size)
+    return oracle.staged_then_scatter(pool, rows, page, off)
+
+
+def _timed_chunks(name, first_chunk, target_s):
+    """Chunks of _CPU_CHUNK tokens (cycling over the sample from `first_chunk` on) for
+    about target_s of wall time; returns (tokens, seconds)."""
+    T = _CPU_W[name].T
+    n_chunks = T // _CPU_CHUNK
+    done, i = 0, first_chunk
     t0 = time.perf_counter()
     while True:
-        sl = slice(done % w.T, done % w.T + 256)
-        oracle.forward_gqa(w.qkv[sl], "bf16", "sectioned", 8, 4, 128, w.positions[sl], w.q_norm_w, w.k_norm_w,
-                           w.eps, w.theta)
-        oracle.backward_gqa(w.qkv[sl], "bf16", "sectioned", 8, 4, 128, w.positions[sl], w.q_norm_w,
-                            w.k_norm_w, w.eps, w.theta, w.dq[sl], w.dk[sl], w.dv[sl])
-        done += 256
+        c = i % n_chunks
+        done += _oracle_gqa(name, c * _CPU_CHUNK, (c + 1) * _CPU_CHUNK)
+        i += 1
         el = time.perf_counter() - t0
         if el >= target_s:
-            break
+            return done, el
+
+
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(target_s: float = 2.5, reps: int = 5):
+    """The oracle (NumPy fp64) on a bounded sample of every workload, on one host core and on
+    all of this process's host cores (token shards over one forked worker process per core,
+    at most 16), in the same run as the GPU figures.
+
+    Large workloads (training fwd+bwd, prefill): 256-token chunks for about target_s each way,
+    scaled to us per 16384-token layer.  Small workloads (decode, the MLA paged store): the
+    median of `reps` calls on the whole batch.  Runs before the GPU is touched, so the workers
+    are forked from a process that has not initialised HIP.
+    """
+    import multiprocessing as mp
+    import statistics
+
+    from threadpoolctl import threadpool_limits
+
+    import oracle  # noqa: F401  (imported once here, inherited by the forked workers)
+
+    _CPU_W.update(_cpu_workloads())
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    fwd_b, bwd_b = gqa_bytes(1, 32, 8, 128, 2)
+    out = {}
+    with threadpool_limits(1), mp.get_context("fork").Pool(cores) as pool:
+        pool.starmap(_oracle_gqa, [("decode_T1", 0, 1)] * cores)  # every worker up and importing
+        for name in ("train_fwd_plus_bwd", "prefill_rope", "prefill_nope"):
+            tok1, el1 = _timed_chunks(name, 0, target_s)
+            res = pool.starmap(_timed_chunks, [(name, i, target_s) for i in range(cores)])
+            tokn, eln = sum(r[0] for r in res), max(r[1] for r in res)
+            out[name] = {"1_core": round(el1 / tok1 * 16384 * 1e6, 1),
+                         f"{cores}_cores": round(eln / tokn * 16384 * 1e6, 1),
+                         "tokens_1_core": tok1, f"tokens_{cores}_cores": tokn}
+        for T in (1, 8, 64, 256):
+            name = f"decode_T{T}"
+            shards = [(name, T * i // min(cores, T), T * (i + 1) // min(cores, T)) for i in range(min(cores, T))]
+            one, many = [], []
+            for _ in range(reps):
+                t0 = time.perf_counter()
+                _oracle_gqa(name, 0, T)
+                one.append(time.perf_counter() - t0)
+                t0 = time.perf_counter()
+                pool.starmap(_oracle_gqa, shards)
+                many.append(time.perf_counter() - t0)
+            out[name] = {"1_core": round(statistics.median(one) * 1e6, 1),
+                         f"{cores}_cores": round(statistics.median(many) * 1e6, 1)}
+        lw = _CPU_W["mla_latent_paged_B4xT16"]
+        lpool = np.zeros((lw.num_pages, lw.page_size, 576), dtype=np.uint16)
+        shards = [(lw.T * i // cores, lw.T * (i + 1) // cores) for i in range(cores)]
+        one, many = [], []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            _oracle_latent_store(lpool, _oracle_latent_rows(0, lw.T))
+            one.append(time.perf_counter() - t0)
+            t0 = time.perf_counter()
+            _oracle_latent_store(lpool, np.concatenate(pool.starmap(_oracle_latent_rows, shards)))
+            many.append(time.perf_counter() - t0)
+        out["mla_latent_paged_B4xT16"] = {"1_core": round(statistics.median(one) * 1e6, 1),
+                                          f"{cores}_cores": round(statistics.median(many) * 1e6, 1)}
+    step_b = fwd_b + bwd_b
+    tr = out["train_fwd_plus_bwd"]
     return {
-        "value": round((fwd_b + bwd_b) * done / el / 1e9, 4),
+        "value": round(step_b * 16384 / (tr[f"{cores}_cores"] * 1e-6) / 1e9, 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": cores,
         "kind": "oracle",
-        "sample": f"{done} tokens of the same workload (sectioned 32q/8kv/D128 bf16, fwd+bwd) in "
-                  f"{el:.1f} s on one host core (NumPy fp64, single-threaded ufuncs); "
-                  f"{el / done * 16384 * 1e3:.0f} ms per 16384-token layer",
+        "sample": (f"training fwd+bwd (sectioned 32q/8kv/D128 bf16): {tr[f'tokens_{cores}_cores']} tokens in "
+                   f"256-token chunks of the generator's 2048-token batch over {cores} forked processes, "
+                   f"~{target_s:.1f} s; also prefill RoPE/NoPE the same way, decode T=1/8/64/256 and the MLA "
+                   f"paged store (median of {reps} calls); NumPy fp64, BLAS limited to 1 thread per process"),
+        "cpu_model": _cpu_model(),
+        "host_cores_visible": len(os.sched_getaffinity(0)),
+        "single_core": {"value": round(step_b * 16384 / (tr["1_core"] * 1e-6) / 1e9, 4), "unit": "GB/s",
+                        "cores": 1},
+        "us_per_layer": out,
     }
 
 
@@ -256,13 +394,43 @@ def proj_extras(stream, n: int = 20):
     return res
 
 
+LEGS = ("prefill", "decode", "mla", "drafter", "muon", "proj")
+
+
+def settle_clocks(step, min_ms: float = 250.0, max_ms: float = 3000.0, batch: int = 25, tol: float = 0.01):
+    """Runs full steps until the GPU's clocks have settled: at least min_ms of back-to-back
+    steps, then until two successive batches of `batch` steps agree within `tol` (at most
+    max_ms).  An idle GPU takes tens of milliseconds to reach its working clocks, so a
+    handful of warm-up steps would time the ramp.  Returns (ms, steps, last batch's ms/step)."""
+    import torch
+
+    t_start = time.perf_counter()
+    prev, n = None, 0
+    while True:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(batch):
+            step(n)
+            n += 1
+        torch.cuda.synchronize()
+        per = (time.perf_counter() - t0) / batch
+        el = (time.perf_counter() - t_start) * 1e3
+        if el >= max_ms or (el >= min_ms and prev is not None and abs(per - prev) <= tol * prev):
+            return el, n, per * 1e3
+        prev = per
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--no-extras", action="store_true", help="only the training step")
+    ap.add_argument("--legs", default="all",
+                    help="comma list of extra legs after the training step: " + ",".join(LEGS) + " (or all, none)")
+    ap.add_argument("--no-extras", action="store_true", help="only the training step (same as --legs none)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--settle-ms", type=float, default=250.0,
+                    help="minimum clock-settling time before the warm-up steps (0: none, e.g. for counter runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy exactly 256 MiB device-to-device 3 times (a known-size reference for "
                          "hardware byte counters)")
@@ -271,6 +439,14 @@ def main():
         print("bench.py measures one GPU only: the library has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
+    legs = set(LEGS) if args.legs == "all" else set() if args.legs == "none" else set(args.legs.split(","))
+    if legs - set(LEGS):
+        ap.error(f"unknown legs {sorted(legs - set(LEGS))}")
+    if args.no_extras:
+        legs = set()
+
+    # the oracle first: its worker processes are forked before this process touches the GPU
+    cpu = None if args.no_cpu else cpu_baseline()
 
     import torch
 
@@ -318,17 +494,22 @@ def main():
         qk.backward(s["qkv"], pos, wq, wk, s["dq"], s["dk"], s["dv"], out=(s["dqkv"], s["dwq"], s["dwk"]), **kw)
 
     stream = torch.cuda.current_stream()
-    for i in range(args.warmup):
+
+    def step(i):
         fwd(sets[i % 3])
         bwd(sets[(i - 1) % 3])
+
+    settle_ms, settle_steps, settle_last = (settle_clocks(step, min_ms=args.settle_ms) if args.settle_ms > 0
+                                            else (0.0, 0, 0.0))
+    for i in range(args.warmup):
+        step(i)
 
     # the timed region: exactly K steps, nothing else enqueued between them
     K = args.steps
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        fwd(sets[i % 3])
-        bwd(sets[(i - 1) % 3])
+        step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
@@ -368,7 +549,7 @@ def main():
         "copy_ceiling_GBps": round(fwd_b / (copy_ms * 1e-3) / 1e9, 1),
     }
 
-    if not args.no_extras:
+    if "prefill" in legs:
         # ------------------------------------------------------------ Muse prefill, RoPE and NoPE layers
         for rope in (True, False):
             pw = prefill_interleaved(16384, rope=rope)
@@ -396,29 +577,54 @@ def main():
             extras[f"prefill_{tag}_GBps"] = round(pb / (us * 1e-6) / 1e9, 1)
             del bufs, outs, pq
 
-        # ------------------------------------------------------------ decode, HIP-graph replays
-        # one graph holds CALLS forward calls (as a decode step holds every layer's), so the
+    # ------------------------------------------------------------ decode, HIP-graph replays
+    CALLS = 32  # forward calls per graph in the latency-bound legs
+    if "decode" in legs:
+            # one graph holds CALLS forward calls (as a decode step holds every layer's), so the
         # per-call figure is GPU time plus the in-graph launch gap, not host submission
-        CALLS = 32
-        for Td in (1, 8, 64, 256):
-            dw = decode_interleaved(Td)
-            dq_ = dev_bf16(dw.qkv)
-            dp = torch.from_numpy(dw.positions).to(dev)
-            dwq_, dwk_ = dev_bf16(dw.q_norm_w), dev_bf16(dw.k_norm_w)
-            o = (torch.empty((Td, 128, 64), dtype=torch.bfloat16, device=dev),
-                 torch.empty((Td, 16, 64), dtype=torch.bfloat16, device=dev),
-                 torch.empty((Td, 16, 64), dtype=torch.bfloat16, device=dev))
-            dk_ = dict(kind="interleaved", n_kv=16, q_per_kv=8, head_dim=64, eps=1e-6, theta=5e5)
-            side = torch.cuda.Stream()
-            side.wait_stream(stream)
-            with torch.cuda.stream(side):
-                for _ in range(3):
-                    qk.forward(dq_, dp, dwq_, dwk_, out=o, **dk_)
-            stream.wait_stream(side)
+            for Td in (1, 8, 64, 256):
+                dw = decode_interleaved(Td)
+                dq_ = dev_bf16(dw.qkv)
+                dp = torch.from_numpy(dw.positions).to(dev)
+                dwq_, dwk_ = dev_bf16(dw.q_norm_w), dev_bf16(dw.k_norm_w)
+                o = (torch.empty((Td, 128, 64), dtype=torch.bfloat16, device=dev),
+                     torch.empty((Td, 16, 64), dtype=torch.bfloat16, device=dev),
+                     torch.empty((Td, 16, 64), dtype=torch.bfloat16, device=dev))
+                dk_ = dict(kind="interleaved", n_kv=16, q_per_kv=8, head_dim=64, eps=1e-6, theta=5e5)
+                side = torch.cuda.Stream()
+                side.wait_stream(stream)
+                with torch.cuda.stream(side):
+                    for _ in range(3):
+                        qk.forward(dq_, dp, dwq_, dwk_, out=o, **dk_)
+                stream.wait_stream(side)
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for _ in range(CALLS):
+                        qk.forward(dq_, dp, dwq_, dwk_, out=o, **dk_)
+                for _ in range(5):
+                    g.replay()
+                n = 20
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(n):
+                    g.replay()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                extras[f"decode_T{Td}_us"] = round(e0.elapsed_time(e1) / (n * CALLS) * 1e3, 2)
+                del g
+
+    # ------------------------------------------------------------ MLA latent rows into the paged pool
+    if "mla" in legs:
+            lw = latent_paged()
+            rows, lp, lwk = dev_bf16(lw.qkv), torch.from_numpy(lw.positions).to(dev), dev_bf16(lw.k_norm_w)
+            bt = torch.from_numpy(lw.block_table).to(dev)
+            pool = torch.zeros((lw.num_pages, lw.page_size, 576), dtype=torch.bfloat16, device=dev)
+            for _ in range(3):
+                qk.forward_latent_paged(rows, lp, lwk, bt, pool, tokens_per_req=lw.tokens_per_req)
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 for _ in range(CALLS):
-                    qk.forward(dq_, dp, dwq_, dwk_, out=o, **dk_)
+                    qk.forward_latent_paged(rows, lp, lwk, bt, pool, tokens_per_req=lw.tokens_per_req)
             for _ in range(5):
                 g.replay()
             n = 20
@@ -428,40 +634,20 @@ def main():
                 g.replay()
             e1.record(stream)
             torch.cuda.synchronize()
-            extras[f"decode_T{Td}_us"] = round(e0.elapsed_time(e1) / (n * CALLS) * 1e3, 2)
-            del g
+            extras["mla_latent_paged_B4xT16_us"] = round(e0.elapsed_time(e1) / (n * CALLS) * 1e3, 2)
+            del pool, g
 
-        # ------------------------------------------------------------ MLA latent rows into the paged pool
-        lw = latent_paged()
-        rows, lp, lwk = dev_bf16(lw.qkv), torch.from_numpy(lw.positions).to(dev), dev_bf16(lw.k_norm_w)
-        bt = torch.from_numpy(lw.block_table).to(dev)
-        pool = torch.zeros((lw.num_pages, lw.page_size, 576), dtype=torch.bfloat16, device=dev)
-        for _ in range(3):
-            qk.forward_latent_paged(rows, lp, lwk, bt, pool, tokens_per_req=lw.tokens_per_req)
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for _ in range(CALLS):
-                qk.forward_latent_paged(rows, lp, lwk, bt, pool, tokens_per_req=lw.tokens_per_req)
-        for _ in range(5):
-            g.replay()
-        n = 20
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(n):
-            g.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        extras["mla_latent_paged_B4xT16_us"] = round(e0.elapsed_time(e1) / (n * CALLS) * 1e3, 2)
-        del pool, g
+    # ------------------------------------------------------------ MLA drafter layers: kv path beside q path
+    if "drafter" in legs:
+            extras["mla_drafter"] = drafter_extras(dev_bf16, stream)
 
-        # ------------------------------------------------------------ MLA drafter layers: kv path beside q path
-        extras["mla_drafter"] = drafter_extras(dev_bf16, stream)
+    # ------------------------------------------------------------ per-head Newton-Schulz on the fused weight
+    if "muon" in legs:
+            extras["muon_newton_schulz"] = muon_extras(stream)
 
-        # ------------------------------------------------------------ per-head Newton-Schulz on the fused weight
-        extras["muon_newton_schulz"] = muon_extras(stream)
-
-        # ------------------------------------------------------------ QKV projection with the region in its epilogue
-        extras["fused_qkv_projection"] = proj_extras(stream)
+    # ------------------------------------------------------------ QKV projection with the region in its epilogue
+    if "proj" in legs:
+            extras["fused_qkv_projection"] = proj_extras(stream)
 
     out = {
         "metric": METRIC,
@@ -470,6 +656,9 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        # before the counted warm-up: full steps until the clocks settled (not timed, not counted)
+        "settle": {"ms": round(settle_ms, 1), "steps": settle_steps,
+                   "last_batch_us_per_step": round(settle_last * 1e3, 2)},
         "ms_per_step": round(ms_per_step, 4),
         "us_per_layer": round(ms_per_step * 1e3, 2),
         "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBS, 1),
@@ -495,8 +684,11 @@ def main():
         },
         "extras": extras,
     }
-    if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline()
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
+        # the oracle's time beside each GPU figure it matches
+        for name, t in cpu["us_per_layer"].items():
+            extras[f"{name}_oracle_us"] = {k: v for k, v in t.items() if not k.startswith("tokens")}
     print(json.dumps(out), flush=True)
 
 
