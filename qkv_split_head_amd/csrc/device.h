@@ -70,12 +70,22 @@ __device__ __forceinline__ float head_sum(float v) {
   return v;
 }
 
+// A lane permutation in which every lane has a source lane (the mirrors):
+// bound_ctrl set and full masks, so the old value is never read and the
+// compiler folds the move into the instruction that uses it (v_mul_f32_dpp)
+// instead of zeroing a register and moving into it.
+template <int CTRL>
+__device__ __forceinline__ float dpp_perm(float v) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
 // Value held by the rotate-half partner lane (lane LPH-1-li of the same head).
 template <int LPH>
 __device__ __forceinline__ float partner(float v) {
   static_assert(LPH == 8 || LPH == 16 || LPH == 32, "head lane count");
-  if constexpr (LPH == 8) return dpp<kRowHalfMirror>(v);
-  else if constexpr (LPH == 16) return dpp<kRowMirror>(v);
+  if constexpr (LPH == 8) return dpp_perm<kRowHalfMirror>(v);
+  else if constexpr (LPH == 16) return dpp_perm<kRowMirror>(v);
   else return swizzle<kSwzXor31>(v);
 }
 
@@ -103,11 +113,12 @@ __device__ __forceinline__ void unpack(const uint4& c, float (&f)[4]) {
   f[3] = __uint_as_float(c.w);
 }
 
-// Round two fp32 values to bf16 (nearest-even, v_cvt_pk_bf16_f32) and pack them.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// Round two fp32 values to bf16 (nearest-even) and pack them: one two-source
+// v_cvt_pk_bf16_f32 (two one-value conversions cost a shift and an or more).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const uint32_t a = __builtin_bit_cast(uint16_t, static_cast<__bf16>(lo));
-  const uint32_t b = __builtin_bit_cast(uint16_t, static_cast<__bf16>(hi));
-  return a | (b << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 __device__ __forceinline__ uint4 pack(const float (&f)[8]) {

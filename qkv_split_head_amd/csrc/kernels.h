@@ -158,6 +158,17 @@ __device__ __forceinline__ int64_t paged_slot(const int32_t* bt, int32_t bt_stri
   return static_cast<int64_t>(page) * page_size + (p - pi * page_size);
 }
 
+// What the heads of one wave iteration are, decided once for the wave: all q
+// (0), all k (1), all v (2), or a mix (3).  A uniform iteration takes a body
+// compiled for its one head type: one weight, one output, no per-lane selects,
+// and a v iteration does no arithmetic at all.  Lane 0 always holds a head of
+// the row; lanes past the last head do not count.
+enum : int { kAllQ = 0, kAllK = 1, kAllV = 2, kMixed = 3 };
+__device__ __forceinline__ int iter_kind(int h, int heads, int type) {
+  const int first = __builtin_amdgcn_readfirstlane(type);
+  return __builtin_amdgcn_ballot_w64(h < heads && type != first) == 0 ? first : kMixed;
+}
+
 template <typename IO, int D>
 struct Geo {
   static constexpr int EPC = Chunk<IO>::EPC;
@@ -178,6 +189,51 @@ __device__ __forceinline__ bool wave_unit(const GqaArgs& a, int U, int waves_per
 }
 
 // ------------------------------------------------------------------ forward
+
+// One forward iteration of the lane's head h (type, idx from map_head; kind
+// from iter_kind): normalise, rotate, round once and store to q, k or v (a v
+// head stores the loaded bits).  kv_tok is the token's k/v row (its pool slot
+// when paged, -1 when the table does not map it).
+template <typename IO, int D, bool ROPE>
+__device__ __forceinline__ void fwd_iter(int kind, const uint4& xb, const uint4& wq_raw, const uint4& wk_raw,
+                                         const float (&cs)[Geo<IO, D>::EPC], const float (&sn)[Geo<IO, D>::EPC],
+                                         float eps, float inv_d, int h, int heads, int type, int idx, int cb,
+                                         uint8_t* q, uint8_t* k, uint8_t* v, int64_t t, int64_t kv_tok, int n_q,
+                                         int n_kv) {
+  using G = Geo<IO, D>;
+  constexpr int EPC = G::EPC, LPH = G::LPH, HB = G::HB;
+  if (kind == kAllV) {  // wave-uniform: a copy, no arithmetic
+    if (h < heads && kv_tok >= 0) st_stream(v + (kv_tok * n_kv + idx) * HB + cb, xb);
+    return;
+  }
+  float x[EPC];
+  unpack(xb, x);
+  float ss = 0.0f;
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) ss = fmaf(x[e], x[e], ss);
+  ss = head_sum<LPH>(ss);
+  const float r = rsqrtf(ss * inv_d + eps);
+  float w[EPC], y[EPC];
+  unpack(type == 0 ? wq_raw : wk_raw, w);
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) y[e] = x[e] * r * w[e];
+  if constexpr (ROPE) {
+    float z[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) z[e] = fmaf(y[e], cs[e], partner<LPH>(y[e]) * sn[e]);
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) y[e] = z[e];
+  }
+  if (kind == kAllQ) {  // wave-uniform branches: one output, no per-lane selects
+    if (h < heads) st_stream(q + (t * n_q + idx) * HB + cb, pack(y));
+  } else if (kind == kAllK) {
+    if (h < heads && kv_tok >= 0) st_stream(k + (kv_tok * n_kv + idx) * HB + cb, pack(y));
+  } else {
+    const uint4 out = type == 2 ? xb : pack(y);
+    uint8_t* dst = type == 0 ? q + (t * n_q + idx) * HB : (type == 1 ? k : v) + (kv_tok * n_kv + idx) * HB;
+    if (h < heads && (type == 0 || kv_tok >= 0)) st_stream(dst + cb, out);
+  }
+}
 
 // U iterations per work unit, DEPTH of their loads in flight at once: (kFwdU,
 // kFwdDepth) for streaming batches, (1, 1) for small batches, where the
@@ -229,28 +285,8 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_gqa_kernel(const GqaArgs a)
     const int h = (it0 + j) * HPI + hs;
     int type, idx;
     map_head(a, h, type, idx);
-    float x[EPC];
-    unpack(buf[j], x);
-    float ss = 0.0f;
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) ss = fmaf(x[e], x[e], ss);
-    ss = head_sum<LPH>(ss);
-    const float r = rsqrtf(ss * a.inv_d + a.eps);
-    float w[EPC], y[EPC];
-    unpack(type == 0 ? wq_raw : wk_raw, w);
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) y[e] = x[e] * r * w[e];
-    if constexpr (ROPE) {
-      float z[EPC];
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) z[e] = fmaf(y[e], cs[e], partner<LPH>(y[e]) * sn[e]);
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) y[e] = z[e];
-    }
-    const uint4 out = type == 2 ? buf[j] : pack(y);
-    uint8_t* dst = type == 0 ? a.q + (t * a.n_q + idx) * HB
-                             : (type == 1 ? a.k : a.v) + (kv_tok * a.n_kv + idx) * HB;
-    if (h < a.heads && (type == 0 || kv_tok >= 0)) st_stream(dst + cb, out);
+    fwd_iter<IO, D, ROPE>(iter_kind(h, a.heads, type), buf[j], wq_raw, wk_raw, cs, sn, a.eps, a.inv_d, h, a.heads,
+                          type, idx, cb, a.q, a.k, a.v, t, kv_tok, a.n_q, a.n_kv);
     if (j + DEPTH < U) {
       __builtin_amdgcn_sched_barrier(0);
       buf[j + DEPTH] = ld_stream(row + min((it0 + j + DEPTH) * HPI + hs, a.heads - 1) * HB + cb);
@@ -286,6 +322,77 @@ __device__ __forceinline__ void bwd_load(const GqaArgs a, int64_t t, int h, cons
                                : (type == 1 ? a.dk : a.dv) + (t * a.n_kv + idx) * HB;
   gb = ld_stream(g + cb);
   xb = ld_stream(type != 2 ? row + h * HB + cb : a.wq + cb);
+}
+
+// One backward iteration of the lane's head h (type from map_head; kind from
+// iter_kind): the cotangent rotated back, the RMSNorm backward recomputed from
+// the packed input, the packed grad stored in dqkv (a v head stores the loaded
+// cotangent bits) and the head's weight-grad terms u x^ added to the lane's sums.
+template <typename IO, int D, bool ROPE>
+__device__ __forceinline__ void bwd_iter(int kind, const uint4& xb, const uint4& gb, const uint4& wq_raw,
+                                         const uint4& wk_raw, const float (&cs)[Geo<IO, D>::EPC],
+                                         const float (&sn)[Geo<IO, D>::EPC], float eps, float inv_d, int h, int heads,
+                                         int type, uint8_t* drow, int cb, float (&accq)[Geo<IO, D>::EPC],
+                                         float (&acck)[Geo<IO, D>::EPC]) {
+  using G = Geo<IO, D>;
+  constexpr int EPC = G::EPC, LPH = G::LPH, HB = G::HB;
+  if (kind == kAllV) {  // wave-uniform: the cotangent is the grad, no arithmetic
+    if (h < heads) st_stream(drow + h * HB + cb, gb);
+    return;
+  }
+  float x[EPC], g[EPC];
+  unpack(xb, x);
+  unpack(gb, g);
+  float ss = 0.0f;
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) ss = fmaf(x[e], x[e], ss);
+  ss = head_sum<LPH>(ss);
+  const float r = rsqrtf(ss * inv_d + eps);
+  float uu[EPC];
+  if constexpr (ROPE) {
+    // transpose of the forward rotation: u = g cos - partner(g) * (signed sin)
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) uu[e] = fmaf(g[e], cs[e], -partner<LPH>(g[e]) * sn[e]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) uu[e] = g[e];
+  }
+  float w[EPC], xh[EPC], av[EPC];
+  unpack(type == 0 ? wq_raw : wk_raw, w);
+  float dot = 0.0f;
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) {
+    xh[e] = x[e] * r;
+    av[e] = uu[e] * w[e];
+    dot = fmaf(av[e], xh[e], dot);
+  }
+  dot = head_sum<LPH>(dot);
+  const float m = dot * inv_d;
+  float dx[EPC];
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) dx[e] = r * fmaf(-xh[e], m, av[e]);
+  if (h < heads) {
+    if (kind == kAllQ) {  // wave-uniform branches: one sum, no per-lane selects
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) accq[e] = fmaf(uu[e], xh[e], accq[e]);
+      st_stream(drow + h * HB + cb, pack(dx));
+    } else if (kind == kAllK) {
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acck[e] = fmaf(uu[e], xh[e], acck[e]);
+      st_stream(drow + h * HB + cb, pack(dx));
+    } else {
+      // value selects, not a choice of array (that would move both
+      // accumulators to scratch); a select also keeps a v head's unused
+      // term (NaN when eps = 0) out of the sums
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        const float term = uu[e] * xh[e];
+        accq[e] += type == 0 ? term : 0.0f;
+        acck[e] += type == 1 ? term : 0.0f;
+      }
+      st_stream(drow + h * HB + cb, type == 2 ? gb : pack(dx));
+    }
+  }
 }
 
 template <typename IO, int D, bool ROPE>
@@ -333,49 +440,8 @@ __global__ __launch_bounds__(kBwdBlockThreads) void bwd_gqa_kernel(const GqaArgs
       const int h = (it0 + j) * HPI + hs;
       int type, idx;
       map_head(a, h, type, idx);
-      float x[EPC], g[EPC];
-      unpack(xb[j], x);
-      unpack(gb[j], g);
-      float ss = 0.0f;
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) ss = fmaf(x[e], x[e], ss);
-      ss = head_sum<LPH>(ss);
-      const float r = rsqrtf(ss * a.inv_d + a.eps);
-      float uu[EPC];
-      if constexpr (ROPE) {
-        // transpose of the forward rotation: u = g cos - partner(g) * (signed sin)
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) uu[e] = fmaf(g[e], cs[e], -partner<LPH>(g[e]) * sn[e]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) uu[e] = g[e];
-      }
-      float w[EPC], xh[EPC], av[EPC];
-      unpack(type == 0 ? wq_raw : wk_raw, w);
-      float dot = 0.0f;
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) {
-        xh[e] = x[e] * r;
-        av[e] = uu[e] * w[e];
-        dot = fmaf(av[e], xh[e], dot);
-      }
-      dot = head_sum<LPH>(dot);
-      const float m = dot * a.inv_d;
-      float dx[EPC];
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) dx[e] = r * fmaf(-xh[e], m, av[e]);
-      if (h < a.heads) {
-        // value selects, not a choice of array (that would move both
-        // accumulators to scratch); a select also keeps a v head's unused
-        // term (NaN when eps = 0) out of the sums
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) {
-          const float term = uu[e] * xh[e];
-          accq[e] += type == 0 ? term : 0.0f;
-          acck[e] += type == 1 ? term : 0.0f;
-        }
-        st_stream(drow + h * HB + cb, type == 2 ? gb[j] : pack(dx));
-      }
+      bwd_iter<IO, D, ROPE>(iter_kind(h, a.heads, type), xb[j], gb[j], wq_raw, wk_raw, cs, sn, a.eps, a.inv_d, h,
+                            a.heads, type, drow, cb, accq, acck);
       if (j + kBwdDepth < U) {
         __builtin_amdgcn_sched_barrier(0);
         bwd_load<HB>(a, t, (it0 + j + kBwdDepth) * HPI + hs, row, cb, xb[j + kBwdDepth], gb[j + kBwdDepth]);
@@ -384,22 +450,15 @@ __global__ __launch_bounds__(kBwdBlockThreads) void bwd_gqa_kernel(const GqaArgs
     }
   }
 
-  // lanes holding the same chunk (same li) -> lanes 0..LPH-1 of the wave
+  // Every lane's sums go to LDS as they are (contiguous EPC values per lane,
+  // 16-byte writes): no cross-lane shuffles, which would cost a chain of
+  // LDS-crossbar permutes per value.  After the barrier each value's sum runs
+  // over the block's waves and each wave's HPI head slots.
+  __shared__ float red[kBwdWavesPerBlock * HPI][2][D];
 #pragma unroll
-  for (int off = LPH; off < kWave; off <<= 1) {
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) {
-      accq[e] += __shfl_xor(accq[e], off, kWave);
-      acck[e] += __shfl_xor(acck[e], off, kWave);
-    }
-  }
-  __shared__ float red[kBwdWavesPerBlock][2][D];
-  if (hs == 0) {
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) {
-      red[wave][0][c * EPC + e] = accq[e];
-      red[wave][1][c * EPC + e] = acck[e];
-    }
+  for (int e = 0; e < EPC; ++e) {
+    red[wave * HPI + hs][0][c * EPC + e] = accq[e];
+    red[wave * HPI + hs][1][c * EPC + e] = acck[e];
   }
   // a barrier that orders LDS only: __syncthreads() would also make every
   // wave wait for its streaming stores to be acknowledged first
@@ -410,7 +469,7 @@ __global__ __launch_bounds__(kBwdBlockThreads) void bwd_gqa_kernel(const GqaArgs
   for (int i = threadIdx.x; i < 2 * D; i += kBwdBlockThreads) {
     float s = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kBwdWavesPerBlock; ++w) s += red[w][i / D][i % D];
+    for (int k = 0; k < kBwdWavesPerBlock * HPI; ++k) s += red[k][i / D][i % D];
     atomicAdd(slot + i, s);
   }
 }
