@@ -688,7 +688,8 @@ def main():
             "buffer_sets_rotated": 3,
         },
         "roofline": {
-            "kernel": "bwd_gqa_kernel<bf16, D=128, RoPE> (+ its one-block weight-grad fold launch)",
+            "kernel": "one qkvnr_backward call: bwd_gqa_kernel<bf16, D=128, RoPE> + its one-block weight-grad fold "
+                      "(wgrad_fold_kernel), HIP events over the per-launch loop",
             "bound": "hbm",
             "achieved": round(bwd_gbs, 1),
             "peak": PEAK_HBM_GBS,
