@@ -302,8 +302,8 @@ def drafter_extras(dev_bf16, stream, layers_n: int = 4, n: int = 30):
 
 def muon_extras(stream, n: int = 10):
     """One Muon orthogonalisation (5 quintic Newton-Schulz steps) of the Qwen3-8B-like fused
-    q|k|v weight [6144, 4096] (seeded N(0,1)): per head (48 blocks of 128 rows) in bf16 and
-    fp32, and on the whole matrix in bf16 (the full-matrix path, library products only)."""
+    q|k|v weight [6144, 4096] (seeded N(0,1)): per head (48 blocks of 128 rows) in bf16 (one launch a
+    step) and fp32, and on the whole matrix in bf16 (the full-matrix path, library products only)."""
     import torch
     from qkv_split_head_amd.muon import per_head_newton_schulz
 

@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define QKVNR_VERSION 10400 /* major * 10000 + minor * 100 + patch */
+#define QKVNR_VERSION 10500 /* major * 10000 + minor * 100 + patch */
 
 /* Return codes. */
 #define QKVNR_OK 0
@@ -341,6 +341,48 @@ int qkvnr_ns_poly(int32_t dtype, int64_t blocks, int32_t d, float* gram, int32_t
  */
 int qkvnr_ns_update(int64_t blocks, int32_t d, int64_t cols, const void* p, const void* x, void* y,
                     int32_t parts, float* gram, hipStream_t stream);
+
+/*
+ * The whole Newton-Schulz iteration of every block as one d x d matrix M, so
+ * that the result is M G (qkvnr_ns_apply): two passes over the blocks instead
+ * of two a step.  (DeepSpeed page, "What this PR does": each head block is
+ * orthogonalised on its own by Muon's quintic Newton-Schulz steps.)  Each step
+ * multiplies X by P = a I + b X X^T + c (X X^T)^2 with (a, b, c) = (3.4445,
+ * -4.7750, 2.0315), a polynomial in G G^T, so from A'_0 = G G^T / (||G||_F +
+ * eps)^2:  P_k = a I + b A'_k + c A'_k A'_k,  A'_{k+1} = P_k A'_k P_k,
+ * M_{k+1} = P_k M_k,  and M = M_steps * scale / (||G||_F + eps): in exact
+ * arithmetic the same M G as `steps` calls of qkvnr_ns_poly and an update.
+ * Every product is taken from operands split into two bf16 terms (hi + lo,
+ * within 2^-16 of the value) with fp32 accumulation, and M is written as the
+ * same two terms: M's entries grow with the block's condition while M G stays
+ * near orthogonal, so M needs more than bf16's 8 bits.
+ *
+ *   blocks  number of blocks, 0 .. 2^22 (0 is a no-op).
+ *   d       block side: 64 or 128 (others QKVNR_EUNSUPPORTED).
+ *   gram    [blocks, parts, d, d] fp32, 16-byte aligned: G G^T as partial sums
+ *           (qkvnr_gram_partials), added in order; read only.
+ *   parts   1..65535.
+ *   steps   Newton-Schulz steps, 1..64.
+ *   scale   > 0 and finite: the block scale max(1, rows/cols)**0.5.
+ *   eps     >= 0 and finite.
+ *   m       out [blocks, 2, d, d] bf16, 16-byte aligned: hi terms, then lo
+ *           terms, of each block's M; must not overlap gram.
+ */
+int qkvnr_ns_collapse(int64_t blocks, int32_t d, const float* gram, int32_t parts, int32_t steps, float scale,
+                      float eps, void* m, hipStream_t stream);
+
+/*
+ * Y = M X for bf16 blocks with M given as two bf16 terms (qkvnr_ns_collapse's
+ * output): both products are added in fp32 before Y's one rounding to bf16.
+ *
+ *   blocks, d, cols, parts: as for qkvnr_ns_update (d 64 or 128).
+ *   m       [blocks, 2, d, d] bf16, 16-byte aligned.
+ *   x       [blocks, d, cols] bf16, 16-byte aligned.
+ *   y       out [blocks, d, cols] bf16, 16-byte aligned; must not overlap x or m
+ *           (QKVNR_EINVAL).
+ */
+int qkvnr_ns_apply(int64_t blocks, int32_t d, int64_t cols, const void* m, const void* x, void* y, int32_t parts,
+                   hipStream_t stream);
 
 /*
  * The QKV projection with the forward region fused into its epilogue.

@@ -41,6 +41,8 @@ from ._binding import (  # noqa: F401
     qkvnr_forward_paged,
     qkvnr_fused_head_blocks,
     qkvnr_gram_partials,
+    qkvnr_ns_apply,
+    qkvnr_ns_collapse,
     qkvnr_ns_poly,
     qkvnr_ns_update,
     qkvnr_proj_forward,

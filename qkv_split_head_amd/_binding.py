@@ -94,6 +94,11 @@ def lib() -> ctypes.CDLL:
         L.qkvnr_ns_update.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int64, vp, vp, vp, ctypes.c_int32,
                                       vp, vp]
         L.qkvnr_ns_update.restype = ctypes.c_int
+        L.qkvnr_ns_collapse.argtypes = [ctypes.c_int64, ctypes.c_int32, vp, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_float, ctypes.c_float, vp, vp]
+        L.qkvnr_ns_collapse.restype = ctypes.c_int
+        L.qkvnr_ns_apply.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int64, vp, vp, vp, ctypes.c_int32, vp]
+        L.qkvnr_ns_apply.restype = ctypes.c_int
         L.qkvnr_proj_forward.argtypes = [lp, ctypes.c_int64, vp, vp, i32p, vp, vp, ctypes.c_float, ctypes.c_double,
                                          vp, vp, vp, vp]
         L.qkvnr_proj_forward.restype = ctypes.c_int
@@ -271,6 +276,17 @@ def qkvnr_ns_poly(dtype: int, blocks: int, d: int, gram, parts: int, first: bool
 def qkvnr_ns_update(blocks: int, d: int, cols: int, p, x, y, parts: int, gram=None, stream=None) -> None:
     """Call ``qkvnr_ns_update`` (``gram`` None: no Gram partials)."""
     _check(lib().qkvnr_ns_update(blocks, d, cols, _ptr(p), _ptr(x), _ptr(y), parts, _ptr(gram), _stream(stream)))
+
+
+def qkvnr_ns_collapse(blocks: int, d: int, gram, parts: int, steps: int, scale: float, eps: float, m,
+                      stream=None) -> None:
+    """Call ``qkvnr_ns_collapse`` (the whole iteration as M, from the Gram partials of G)."""
+    _check(lib().qkvnr_ns_collapse(blocks, d, _ptr(gram), parts, steps, scale, eps, _ptr(m), _stream(stream)))
+
+
+def qkvnr_ns_apply(blocks: int, d: int, cols: int, m, x, y, parts: int, stream=None) -> None:
+    """Call ``qkvnr_ns_apply`` (Y = (M hi + M lo) X)."""
+    _check(lib().qkvnr_ns_apply(blocks, d, cols, _ptr(m), _ptr(x), _ptr(y), parts, _stream(stream)))
 
 
 def qkvnr_proj_forward(layout: Layout, hidden: int, x, w_qkv, positions, q_norm_w, k_norm_w, eps: float,

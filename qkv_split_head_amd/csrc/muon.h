@@ -274,12 +274,17 @@ __global__ __launch_bounds__(kNsThreads) void ns_poly_kernel(const float* __rest
 // (from X^T buffer c mod 2), stores and adds the Gram products of chunk c - 1 (Y buffer
 // (c - 1) mod 2), writes chunk c + 1's X^T and then chunk c's Y.  A buffer is rewritten only
 // after the barrier that follows its last reads.  64 KB of LDS: two workgroups fit on a CU.
-template <int D, bool GRAM>
+//
+// SPLIT: p holds two bf16 terms per block, [blocks][2][D][D] (hi, then lo), and Y = (hi + lo) X: two
+// products a step, added in fp32 before Y's one rounding (the collapsed iteration's M, whose terms
+// carry about 16 bits).
+template <int D, bool GRAM, bool SPLIT = false>
 __global__ __launch_bounds__(kWave * (D / 32), 2) void ns_update_kernel(const uint16_t* __restrict__ p,
                                                                        const uint16_t* __restrict__ x,
                                                                        uint16_t* __restrict__ y, int cols, int slice,
                                                                        float* __restrict__ gout) {
   static_assert(D == 64 || D == 128, "block sides 64 and 128");
+  static_assert(!(GRAM && SPLIT), "the split product forms no Gram matrices");
   constexpr int T = D / 32, THREADS = kWave * T;
   constexpr int XP = D / 8;                  // 16-byte pieces of an X^T row
   constexpr int YP = kGramChunk / 8;         // 16-byte pieces of a Y row
@@ -296,9 +301,13 @@ __global__ __launch_bounds__(kWave * (D / 32), 2) void ns_update_kernel(const ui
   const int rr = lane % 32, h = lane / 32;
 
   // P operands of this lane: row 32 w + rr, k = 16 s + 8 h + [0, 8)
-  uint4 pf[KS];
+  uint4 pf[KS], pl[SPLIT ? KS : 1];
+  const uint16_t* prow = p + (blk * (SPLIT ? 2 : 1) * D + 32 * w + rr) * D + 8 * h;
 #pragma unroll
-  for (int s = 0; s < KS; ++s) pf[s] = ld16(p + (blk * D + 32 * w + rr) * D + 16 * s + 8 * h);
+  for (int s = 0; s < KS; ++s) {
+    pf[s] = ld16(prow + 16 * s);
+    if constexpr (SPLIT) pl[s] = ld16(prow + D * D + 16 * s);
+  }
 
   const int rg = threadIdx.x / 8, cg = threadIdx.x % 8;
   const uint16_t* xr = x + (blk * D + 4 * rg) * static_cast<int64_t>(cols);
@@ -339,6 +348,9 @@ __global__ __launch_bounds__(kWave * (D / 32), 2) void ns_update_kernel(const ui
       for (int ni = 0; ni < 2; ++ni) {
         const int n = 32 * ni + rr;
         const uint4 af = xb[n * XP + ((2 * s + h) ^ (n & (XP - 1)))];
+        if constexpr (SPLIT)
+          ya[ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af),
+                                                           __builtin_bit_cast(bf16x8_t, pl[s]), ya[ni], 0, 0, 0);
         ya[ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af),
                                                          __builtin_bit_cast(bf16x8_t, pf[s]), ya[ni], 0, 0, 0);
       }
@@ -413,6 +425,245 @@ __global__ __launch_bounds__(kWave * (D / 32), 2) void ns_update_kernel(const ui
       for (int e = 0; e < 16; ++e)
         o[(32 * w + 8 * (e / 4) + 4 * h + e % 4) * D + 32 * t + rr] = acc[t][e];
   }
+}
+
+// The iteration collapsed into one d x d computation per block.  Every step multiplies X by a
+// polynomial in the block's Gram matrix, and every such polynomial commutes with A0 = G G^T, so
+// the iterate after k steps is X_k = M_k X_0 with M_k a polynomial in A0: with A'_0 = A0 / (n + eps)^2
+// (n^2 = trace A0 = ||G||_F^2),
+//   P_k = 3.4445 I - 4.7750 A'_k + 2.0315 A'_k A'_k,   A'_{k+1} = P_k A'_k P_k,   M_{k+1} = P_k M_k,
+// and the result is M G with M = M_steps scale / (n + eps): the same function of G as the steps
+// taken on X (ns_poly_kernel and the update), with two passes over G (its Gram matrix, then M G)
+// instead of two a step.  Every matrix here is a polynomial in A0, hence symmetric, which the
+// products use: product(a, b) takes tile (t, w) = rows 32 t + [0, 32) of a (A operand) against rows
+// 32 w + [0, 32) of b (B operand), a b^T, and lane (rr, h) of wave w reads it transposed, as row
+// r = 32 w + rr, columns c = 32 t + 8 e4 + 4 h + [0, 4) of b a^T, in registers 4 e4 + [0, 4) of tile t:
+// each wave then holds whole rows of every result, which is what its next uses need.
+// Precision: every factor is held as two bf16 terms, hi = bf16(v) and lo = bf16(v - hi) (within
+// 2^-16 |v|), and every product is hi hi + hi lo + lo hi with fp32 accumulation (within about 2^-14
+// of |a| |b|); M goes out in the same two terms, applied as (hi + lo) G by ns_update_kernel<SPLIT>.
+// One bf16 rounding of M (2^-9 relative) would not do: M's entries grow with the block's condition
+// while M G stays near orthogonal, so its rounding errors do not cancel.
+// One workgroup per block (D / 32 waves, wave w owning rows 32 w + [0, 32) of every result).  LDS:
+// the current A'_k (or P_k A'_k) and P_k, each as hi and lo in gram_partials_kernel's layout (chunks
+// of 64 columns, row r's 16-byte piece j at j ^ ((r / 2) mod 8)); M stays in registers and reaches
+// the B operand through a swap between lanes rr and rr + 32.
+template <int D>
+__global__ __launch_bounds__(kWave * (D / 32), 1) void ns_collapse_kernel(const float* __restrict__ gram, int parts,
+                                                                         int steps, float scale, float eps,
+                                                                         uint16_t* __restrict__ m) {
+  static_assert(D == 64 || D == 128, "block sides 64 and 128");
+  constexpr int T = D / 32, THREADS = kWave * T, N = D * D, V = N / 4 / THREADS, KS = D / 16;
+  __shared__ uint4 ra[2][N / 8];  // A'_k, then P_k A'_k: hi, lo
+  __shared__ uint4 rp[2][N / 8];  // P_k: hi, lo
+  __shared__ float tred[T];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+  const int rr = lane % 32, h = lane / 32, sw = (rr >> 1) & 7, r = 32 * w + rr;
+  const int64_t blk = blockIdx.x;
+  auto lds_barrier = [] {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  };
+  auto slot = [](int row, int col) { return (col >> 6) * D * 8 + row * 8 + (((col & 63) >> 3) ^ ((row >> 1) & 7)); };
+  auto rest = [](float v, uint32_t pk, int upper) {  // v minus its bf16 value (the upper or lower half of pk)
+    return v - __uint_as_float(upper ? (pk & 0xffff0000u) : (pk << 16));
+  };
+  // hi and lo of 4 adjacent values (row, col .. col + 3) into a region
+  auto put = [&](uint4 (*reg)[N / 8], int row, int col, float4 v) {
+    const uint2 hi = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+    const uint2 lo = make_uint2(pack_bf16x2(rest(v.x, hi.x, 0), rest(v.y, hi.x, 1)),
+                                pack_bf16x2(rest(v.z, hi.y, 0), rest(v.w, hi.y, 1)));
+    reinterpret_cast<uint2*>(&reg[0][slot(row, col)])[(col >> 2) & 1] = hi;
+    reinterpret_cast<uint2*>(&reg[1][slot(row, col)])[(col >> 2) & 1] = lo;
+  };
+  auto unpack4 = [](uint2 u, float (&f)[4]) {
+    f[0] = __uint_as_float(u.x << 16);
+    f[1] = __uint_as_float(u.x & 0xffff0000u);
+    f[2] = __uint_as_float(u.y << 16);
+    f[3] = __uint_as_float(u.y & 0xffff0000u);
+  };
+  // hi + lo of (row, col .. col + 3)
+  auto get = [&](uint4 (*reg)[N / 8], int row, int col) {
+    float a[4], b[4];
+    unpack4(reinterpret_cast<const uint2*>(&reg[0][slot(row, col)])[(col >> 2) & 1], a);
+    unpack4(reinterpret_cast<const uint2*>(&reg[1][slot(row, col)])[(col >> 2) & 1], b);
+    return make_float4(a[0] + b[0], a[1] + b[1], a[2] + b[2], a[3] + b[3]);
+  };
+  auto split3 = [](f32x16_t acc, bf16x8_t ah, bf16x8_t al, bf16x8_t bh, bf16x8_t bl) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc, 0, 0, 0);
+  };
+  // rows 32 t + [0, 32) of fa against rows r of fb, every tile t
+  auto product = [&](uint4 (*fa)[N / 8], uint4 (*fb)[N / 8], f32x16_t (&acc)[T]) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[t] = f32x16_t{};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int base = (s / 4) * D * 8, pos = (2 * (s % 4) + h) ^ sw;
+      const bf16x8_t bh = __builtin_bit_cast(bf16x8_t, fb[0][base + r * 8 + pos]);
+      const bf16x8_t bl = __builtin_bit_cast(bf16x8_t, fb[1][base + r * 8 + pos]);
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const int ra_ = base + (32 * t + rr) * 8 + pos;
+        acc[t] = split3(acc[t], __builtin_bit_cast(bf16x8_t, fa[0][ra_]), __builtin_bit_cast(bf16x8_t, fa[1][ra_]),
+                        bh, bl);
+      }
+    }
+  };
+  auto tile4 = [](const f32x16_t& a, int e4) { return make_float4(a[4 * e4], a[4 * e4 + 1], a[4 * e4 + 2], a[4 * e4 + 3]); };
+
+  // A0 = ((g0 + g1) + g2) + ...: thread x sums the 4 values at 4 (j THREADS + x), two slices in flight
+  const float* g = gram + blk * parts * N;
+  auto load = [&](int pt, float4 (&v)[V]) {
+    const float4* src = reinterpret_cast<const float4*>(g + static_cast<int64_t>(pt) * N) + threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < V; ++j) v[j] = src[j * THREADS];
+  };
+  auto add = [](float4 (&a)[V], const float4 (&b)[V]) {
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      a[j].x += b[j].x;
+      a[j].y += b[j].y;
+      a[j].z += b[j].z;
+      a[j].w += b[j].w;
+    }
+  };
+  float4 av[V];
+  load(0, av);
+  int pt = 1;
+  for (; pt + 1 < parts; pt += 2) {
+    float4 u0[V], u1[V];
+    load(pt, u0);
+    load(pt + 1, u1);
+    add(av, u0);
+    add(av, u1);
+  }
+  for (; pt < parts; ++pt) {
+    float4 u0[V];
+    load(pt, u0);
+    add(av, u0);
+  }
+  // n^2 = trace A0 in a fixed order: each thread's diagonal values, the wave, then the waves
+  float dg = 0.0f;
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const int u = 4 * (j * THREADS + static_cast<int>(threadIdx.x)), k = u / D - u % D;
+    if (k >= 0 && k < 4) dg += k == 0 ? av[j].x : (k == 1 ? av[j].y : (k == 2 ? av[j].z : av[j].w));
+  }
+  for (int off = kWave / 2; off > 0; off >>= 1) dg += __shfl_xor(dg, off, kWave);
+  if (lane == 0) tred[w] = dg;
+  __syncthreads();
+  float n2 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < T; ++i) n2 += tred[i];
+  const float norm_inv = 1.0f / (sqrtf(n2) + eps), a2s = norm_inv * norm_inv;
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const int u = 4 * (j * THREADS + static_cast<int>(threadIdx.x));
+    put(ra, u / D, u % D, make_float4(av[j].x * a2s, av[j].y * a2s, av[j].z * a2s, av[j].w * a2s));
+  }
+  lds_barrier();
+
+  float4 mr[T][4];  // row r of M: columns 32 t + 8 e4 + 4 h + [0, 4)
+  f32x16_t acc[T];
+  for (int k = 0; k < steps; ++k) {
+    // P_k = 3.4445 I - 4.7750 A' + 2.0315 A' A'
+    product(ra, ra, acc);
+    float4 pr[T][4];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int c = 32 * t + 8 * e4 + 4 * h;
+        const float4 a1 = get(ra, r, c), a2 = tile4(acc[t], e4);
+        float4 pv = make_float4(fmaf(kNsC, a2.x, kNsB * a1.x), fmaf(kNsC, a2.y, kNsB * a1.y),
+                                fmaf(kNsC, a2.z, kNsB * a1.z), fmaf(kNsC, a2.w, kNsB * a1.w));
+        const int dd = r - c;  // the diagonal element of this row, if among these 4 columns
+        if (dd == 0) pv.x += kNsA;
+        if (dd == 1) pv.y += kNsA;
+        if (dd == 2) pv.z += kNsA;
+        if (dd == 3) pv.w += kNsA;
+        pr[t][e4] = pv;
+        put(rp, r, c, pv);
+      }
+    lds_barrier();
+    if (k == 0) {
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) mr[t][e4] = pr[t][e4];
+    } else {  // M = P_k M: rows of P (LDS) against rows r of M (registers)
+      // B operand of k-step s: row r, columns 16 s + 8 h + [0, 8), i.e. piece 2 s + h, of which this lane
+      // holds half h; the other half comes from lane rr + 32 (h ^ 1), which sends its half of that piece
+#pragma unroll
+      for (int t = 0; t < T; ++t) acc[t] = f32x16_t{};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const float4 e = mr[s / 2][2 * (s % 2)], o = mr[s / 2][2 * (s % 2) + 1];  // pieces 2 s and 2 s + 1
+        const float4 own = h ? o : e, send = h ? e : o;
+        const float4 got = make_float4(__shfl_xor(send.x, 32, kWave), __shfl_xor(send.y, 32, kWave),
+                                       __shfl_xor(send.z, 32, kWave), __shfl_xor(send.w, 32, kWave));
+        const float4 lo4 = h ? got : own, hi4 = h ? own : got;  // columns 8 (2 s + h) + [0, 4) and + [4, 8)
+        const float v[8] = {lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
+        uint32_t bh[4], bl[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          bh[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+          bl[i] = pack_bf16x2(rest(v[2 * i], bh[i], 0), rest(v[2 * i + 1], bh[i], 1));
+        }
+        const bf16x8_t bhv = __builtin_bit_cast(bf16x8_t, make_uint4(bh[0], bh[1], bh[2], bh[3]));
+        const bf16x8_t blv = __builtin_bit_cast(bf16x8_t, make_uint4(bl[0], bl[1], bl[2], bl[3]));
+        const int base = (s / 4) * D * 8, pos = (2 * (s % 4) + h) ^ sw;
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const int ia = base + (32 * t + rr) * 8 + pos;
+          acc[t] = split3(acc[t], __builtin_bit_cast(bf16x8_t, rp[0][ia]), __builtin_bit_cast(bf16x8_t, rp[1][ia]),
+                          bhv, blv);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) mr[t][e4] = tile4(acc[t], e4);
+    }
+    if (k + 1 < steps) {
+      // A'_{k+1} = (P_k A'_k) P_k.  The transposed reading makes product(a, b) = b a^T, so the factors go in
+      // this order: another one (P_k P_k A'_k, say) is as good in exact arithmetic but not symmetric in
+      // form, and its rounding's antisymmetric part would grow from step to step
+      product(ra, rp, acc);  // P_k A'_k
+      lds_barrier();         // every read of A'_k is done
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) put(ra, r, 32 * t + 8 * e4 + 4 * h, tile4(acc[t], e4));
+      lds_barrier();
+      product(rp, ra, acc);  // (P_k A'_k) P_k
+      lds_barrier();  // every read of P_k A'_k is done
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) put(ra, r, 32 * t + 8 * e4 + 4 * h, tile4(acc[t], e4));
+      lds_barrier();
+    }
+  }
+  // M scale / (n + eps) as hi and lo: m + b 2 D D (hi) and + D D (lo), 8 bytes of each per (t, e4)
+  const float ms = scale * norm_inv;
+  uint16_t* mh = m + blk * 2 * N + r * D;
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      const int c = 32 * t + 8 * e4 + 4 * h;
+      const float v[4] = {mr[t][e4].x * ms, mr[t][e4].y * ms, mr[t][e4].z * ms, mr[t][e4].w * ms};
+      const uint2 hi = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      const uint2 lo = make_uint2(pack_bf16x2(rest(v[0], hi.x, 0), rest(v[1], hi.x, 1)),
+                                  pack_bf16x2(rest(v[2], hi.y, 0), rest(v[3], hi.y, 1)));
+      *reinterpret_cast<uint2*>(mh + c) = hi;
+      *reinterpret_cast<uint2*>(mh + N + c) = lo;
+    }
 }
 
 }  // namespace qkvnr

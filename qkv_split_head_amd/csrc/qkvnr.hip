@@ -735,6 +735,63 @@ int qkvnr_ns_update(int64_t blocks, int32_t d, int64_t cols, const void* p, cons
   return launched("Newton-Schulz update");
 }
 
+int qkvnr_ns_collapse(int64_t blocks, int32_t d, const float* gram, int32_t parts, int32_t steps, float scale,
+                      float eps, void* m, hipStream_t stream) {
+  if (blocks < 0 || blocks > kMaxLaunchBlocks)  // one launch, one workgroup per block
+    return fail(QKVNR_EINVAL, "blocks %lld out of [0, 2^22]", (long long)blocks);
+  if (d != 64 && d != 128) return fail(QKVNR_EUNSUPPORTED, "block side %d: the collapse kernel exists for 64 and 128", d);
+  if (parts < 1 || parts > 65535) return fail(QKVNR_EINVAL, "parts %d out of [1, 65535]", parts);
+  if (steps < 1 || steps > 64) return fail(QKVNR_EINVAL, "steps %d out of [1, 64]", steps);
+  if (!std::isfinite(scale) || scale <= 0.0f) return fail(QKVNR_EINVAL, "scale %g must be finite and > 0", (double)scale);
+  if (!std::isfinite(eps) || eps < 0.0f) return fail(QKVNR_EINVAL, "eps %g must be finite and >= 0", (double)eps);
+  if (blocks == 0) return QKVNR_OK;
+  if (int rc = need16(gram, "gram")) return rc;
+  if (int rc = need16(m, "m")) return rc;
+  const int64_t n = blocks * d * d;
+  if (overlaps({gram, n * parts * 4}, {m, n * 2 * 2})) return fail(QKVNR_EINVAL, "m overlaps gram");
+  int cus = 0;
+  if (int rc = current_device(&cus)) return rc;
+  auto* mo = static_cast<uint16_t*>(m);
+  const dim3 grid(static_cast<uint32_t>(blocks));
+  if (d == 128)
+    hipLaunchKernelGGL((ns_collapse_kernel<128>), grid, dim3(kWave * 4), 0, stream, gram, parts, steps, scale, eps, mo);
+  else
+    hipLaunchKernelGGL((ns_collapse_kernel<64>), grid, dim3(kWave * 2), 0, stream, gram, parts, steps, scale, eps, mo);
+  return launched("Newton-Schulz collapse");
+}
+
+int qkvnr_ns_apply(int64_t blocks, int32_t d, int64_t cols, const void* m, const void* x, void* y, int32_t parts,
+                   hipStream_t stream) {
+  if (blocks < 0 || blocks > kMaxLaunchBlocks)  // one launch, one workgroup (row) per block
+    return fail(QKVNR_EINVAL, "blocks %lld out of [0, 2^22]", (long long)blocks);
+  if (d != 64 && d != 128) return fail(QKVNR_EUNSUPPORTED, "block side %d: the update kernel exists for 64 and 128", d);
+  if (cols < 1 || cols % 8) return fail(QKVNR_EALIGN, "cols %lld must be a positive multiple of 8", (long long)cols);
+  if (cols > (1 << 30)) return fail(QKVNR_EINVAL, "cols %lld above 2^30", (long long)cols);
+  if (parts < 1 || parts > 65535) return fail(QKVNR_EINVAL, "parts %d out of [1, 65535]", parts);
+  if (blocks == 0) return QKVNR_OK;
+  if (blocks > (INT64_MAX / 8) / (int64_t(d) * std::max<int64_t>(cols, 2 * d)))
+    return fail(QKVNR_EINVAL, "%lld blocks of %d x %lld do not fit a 64-bit byte count", (long long)blocks, d,
+                (long long)cols);
+  if (int rc = need16(m, "m")) return rc;
+  if (int rc = need16(x, "x")) return rc;
+  if (int rc = need16(y, "y")) return rc;
+  const int64_t xb = blocks * d * cols * 2, mb = blocks * 2 * d * d * 2;
+  if (int rc = check_disjoint({{y, xb}}, {{x, xb}, {m, mb}})) return rc;
+  int cus = 0;
+  if (int rc = current_device(&cus)) return rc;
+  const int sl = static_cast<int>(((cols + parts - 1) / parts + 15) / 16 * 16);  // as qkvnr_ns_update
+  const dim3 g(static_cast<uint32_t>(blocks), static_cast<uint32_t>(parts));
+  const auto* ms = static_cast<const uint16_t*>(m);
+  const auto* xs = static_cast<const uint16_t*>(x);
+  auto* ys = static_cast<uint16_t*>(y);
+  const int c = static_cast<int>(cols);
+  if (d == 128)
+    hipLaunchKernelGGL((ns_update_kernel<128, false, true>), g, dim3(kWave * 4), 0, stream, ms, xs, ys, c, sl, nullptr);
+  else
+    hipLaunchKernelGGL((ns_update_kernel<64, false, true>), g, dim3(kWave * 2), 0, stream, ms, xs, ys, c, sl, nullptr);
+  return launched("Newton-Schulz apply");
+}
+
 int qkvnr_proj_forward(const qkvnr_layout* layout, int64_t hidden, const void* x, const void* w_qkv,
                        const int32_t* positions, const void* q_norm_w, const void* k_norm_w, float eps,
                        double theta, void* q, void* k, void* v, hipStream_t stream) {

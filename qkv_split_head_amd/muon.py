@@ -9,15 +9,18 @@ is the exact fused total (``qkvnr_fused_head_blocks``); otherwise it is
 declined to the full-matrix path.
 
 Each Newton-Schulz step on the blocks' wide orientation X is X <- P X with
-P = a I + b X X^T + c (X X^T)^2: this library's ``qkvnr_gram_partials`` (the
-Gram matrices with MFMA, reading both factors as rows of X; bf16 blocks of
-side 32..128), ``qkvnr_ns_poly`` (P from the Gram matrices, with the first
-step's Frobenius normalisation and the last step's block scale folded in), and
-the update P X.  For bf16 blocks of side 64 or 128 the update is
-``qkvnr_ns_update``, which also forms the next step's Gram matrices from the
-new X in the same pass, so only the first step reads X for its Gram matrices
-alone.  Other blocks take a plain batched library GEMM.  The blocks never leave
-the ``[blocks, d, in]`` layout between steps.
+P = a I + b X X^T + c (X X^T)^2, a polynomial in G G^T; so the iterate after
+any number of steps is M G with M a polynomial in G G^T.  For bf16 blocks of
+side 64 or 128 the iteration is taken that way, in three launches:
+``qkvnr_gram_partials`` (G G^T with MFMA, reading both factors as rows of G),
+``qkvnr_ns_collapse`` (the steps on d x d matrices, one workgroup per block,
+products from operands split into two bf16 terms) and ``qkvnr_ns_apply``
+(Y = M G, M in two bf16 terms): G is read twice and Y written once, instead of
+two reads and a write a step.  Other bf16 blocks of side 32..128 take the steps
+one by one: ``qkvnr_gram_partials``, ``qkvnr_ns_poly`` (P, with the first
+step's Frobenius normalisation and the last step's block scale folded in) and
+a batched library GEMM for P X; fp32 and other sides take library GEMMs for
+both products.  The blocks never leave the ``[blocks, d, in]`` layout.
 
 ``compute_dtype`` bf16 is Muon's usual precision (GEMMs in bf16 with fp32
 accumulation); fp32 runs the same steps in fp32.
@@ -49,19 +52,20 @@ def _newton_schulz_blocks(X: torch.Tensor, scale: float, steps: int, eps: float)
     """X: [blocks, d, cols] wide blocks (d <= cols), contiguous; returns the orthogonalised blocks."""
     nb, d, cols = X.shape
     dtype = b.DTYPES[X.dtype]
-    P = torch.empty((nb, d, d), dtype=X.dtype, device=X.device)
     own_gram = X.dtype == torch.bfloat16 and d in (32, 64, 96, 128) and cols % 8 == 0
     parts = _gram_parts(nb, cols) if own_gram else 1
     gram = torch.empty((nb, parts, d, d), dtype=torch.float32, device=X.device)
-    if own_gram and d in (64, 128):  # fused update: Y = P X and Y's Gram matrices in one pass
+    if own_gram and d in (64, 128):
+        if steps == 0:
+            return X
+        # collapsed: G's Gram matrices, the whole iteration as M per block, then M G
         b.qkvnr_gram_partials(nb, d, cols, X, parts, gram)
-        bufs = (torch.empty_like(X), torch.empty_like(X))
-        for i in range(steps):
-            b.qkvnr_ns_poly(dtype, nb, d, gram, parts, i == 0, scale if i == steps - 1 else 1.0, eps, P)
-            Y = bufs[i % 2]
-            b.qkvnr_ns_update(nb, d, cols, P, X, Y, parts, gram if i < steps - 1 else None)
-            X = Y
-        return X
+        M = torch.empty((nb, 2, d, d), dtype=X.dtype, device=X.device)
+        b.qkvnr_ns_collapse(nb, d, gram, parts, steps, scale, eps, M)
+        Y = torch.empty_like(X)
+        b.qkvnr_ns_apply(nb, d, cols, M, X, Y, parts)
+        return Y
+    P = torch.empty((nb, d, d), dtype=X.dtype, device=X.device)
     for i in range(steps):
         if own_gram:   # the library kernel reads both factors as rows of X
             b.qkvnr_gram_partials(nb, d, cols, X, parts, gram)
@@ -78,7 +82,8 @@ def per_head_newton_schulz(G: torch.Tensor, n_q: int, n_kv: int, head_dim: int, 
 
     G is ``[(n_q + 2 n_kv) * head_dim, in_features]`` in either block order; the
     result has G's shape and block order and ``compute_dtype`` (default: G's).
-    Each block is scaled by max(1, head_dim / in_features) ** 0.5.
+    Each block is scaled by max(1, head_dim / in_features) ** 0.5.  Every sum is
+    taken in a fixed order: the result does not change from run to run.
     """
     if G.dim() != 2:
         raise ValueError("G must be a 2-D weight")

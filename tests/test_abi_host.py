@@ -362,6 +362,63 @@ def test_ns_update_argument_checks():
     assert call(i0=0, i3=0, i4=0, i5=0, i7=0) == qk.OK   # no blocks: nothing is touched
 
 
+def test_ns_collapse_argument_checks():
+    f = qk.lib().qkvnr_ns_collapse
+    # blocks, d, gram, parts, steps, scale, eps, m
+    ok = [48, 128, A, 5, 5, 1.0, 1e-7, B]
+
+    def call(**change):
+        a = list(ok)
+        for i, v in change.items():
+            a[int(i[1:])] = v
+        return f(*a, None)
+
+    assert call(i0=-1) == qk.EINVAL
+    assert call(i0=(1 << 22) + 1) == qk.EINVAL   # more blocks than one launch holds
+    assert call(i1=32) == qk.EUNSUPPORTED         # sides 64 and 128
+    assert call(i1=96) == qk.EUNSUPPORTED
+    assert call(i3=0) == qk.EINVAL                # parts
+    assert call(i3=65536) == qk.EINVAL
+    assert call(i4=0) == qk.EINVAL                # steps
+    assert call(i4=65) == qk.EINVAL
+    assert call(i5=0.0) == qk.EINVAL              # scale
+    assert call(i5=float("inf")) == qk.EINVAL
+    assert call(i6=-1.0) == qk.EINVAL             # eps
+    assert call(i2=0) == qk.EINVAL                # gram
+    assert call(i2=A + 4) == qk.EALIGN
+    assert call(i7=0) == qk.EINVAL                # m
+    assert call(i7=B + 8) == qk.EALIGN
+    assert call(i7=A + 4096) == qk.EINVAL         # m overlaps gram
+    assert call(i0=0, i2=0, i7=0) == qk.OK        # no blocks: nothing is touched
+
+
+def test_ns_apply_argument_checks():
+    f = qk.lib().qkvnr_ns_apply
+    # blocks, d, cols, m, x, y, parts
+    ok = [48, 128, 4096, A, B, C, 5]
+
+    def call(**change):
+        a = list(ok)
+        for i, v in change.items():
+            a[int(i[1:])] = v
+        return f(*a, None)
+
+    assert call(i0=-1) == qk.EINVAL
+    assert call(i0=(1 << 22) + 1) == qk.EINVAL
+    assert call(i1=96) == qk.EUNSUPPORTED
+    assert call(i2=0) == qk.EALIGN
+    assert call(i2=4100) == qk.EALIGN
+    assert call(i2=(1 << 30) + 8) == qk.EINVAL
+    assert call(i6=0) == qk.EINVAL                # parts
+    assert call(i0=(1 << 31) - 1, i2=1 << 30) == qk.EINVAL   # byte counts past 2^63
+    assert call(i3=A + 8) == qk.EALIGN            # m
+    assert call(i4=B + 8) == qk.EALIGN            # x
+    assert call(i5=C + 8) == qk.EALIGN            # y
+    assert call(i5=B + 4096) == qk.EINVAL         # y overlaps x
+    assert call(i5=A + 64) == qk.EINVAL           # y overlaps m
+    assert call(i0=0, i3=0, i4=0, i5=0) == qk.OK
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     import qkv_split_head_amd._binding as b
     monkeypatch.setattr(b, "_lib", None)

@@ -90,3 +90,4 @@ def test_validation_error_keeps_the_cached_workspace():
         assert bnd._workspaces.get(7) is ws
     finally:
         bnd._workspaces.pop(7, None)
+

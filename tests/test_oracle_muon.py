@@ -3,7 +3,8 @@
 ``oracle.muon`` is checked against things other than its own formulas: the
 singular value decomposition (a matrix polynomial in X X^T applied to X keeps
 the singular vectors and maps each singular value through the scalar
-iteration), the DeepSpeed page's layout facts (sectioned and interleaved fused
+iteration; the same fact lets the library collapse the steps into one matrix
+polynomial in G G^T), the DeepSpeed page's layout facts (sectioned and interleaved fused
 weights give the same update up to the block permutation; 8 query heads over 2
 kv heads are 12 blocks; the Falcon and Conv1D shapes are declined), the scale
 rule's closed forms, and the rank-one case.
@@ -34,6 +35,21 @@ def test_newton_schulz_equals_its_spectral_form(shape):
     U, S, Vt = np.linalg.svd(G, full_matrices=False)
     want = U @ np.diag(_scalar_iterate(S / (np.linalg.norm(G) + 1e-7))) @ Vt
     np.testing.assert_allclose(muon.newton_schulz(G), want, rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("shape,steps", [((16, 40), 5), ((8, 64), 1), ((32, 32), 3), ((12, 200), 7)])
+def test_iteration_collapses_to_a_polynomial_in_the_gram_matrix(shape, steps):
+    # every step multiplies X by a polynomial in G G^T, so the iterate is M G with M from the recurrence
+    # P_k = a I + b A_k + c A_k^2, A_{k+1} = P_k A_k P_k, M_{k+1} = P_k M_k on the normalised Gram matrix:
+    # the reformulation the library's collapsed iteration takes, against the steps as the oracle takes them
+    a, b, c = 3.4445, -4.7750, 2.0315
+    G = np.random.default_rng(sum(shape) + steps).standard_normal(shape)
+    n = np.linalg.norm(G) + 1e-7
+    A, M = G @ G.T / n ** 2, np.eye(shape[0])
+    for _ in range(steps):
+        P = a * np.eye(shape[0]) + b * A + c * A @ A
+        A, M = P @ A @ P, P @ M
+    np.testing.assert_allclose(M @ G / n, muon.newton_schulz(G, steps=steps), rtol=1e-9, atol=1e-12)
 
 
 def test_rank_one_block_has_a_closed_form():
