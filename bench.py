@@ -337,8 +337,11 @@ def muon_extras(stream, n: int = 10):
         "per_head_fp32_us": timed(lambda: per_head_newton_schulz(G, 32, 8, 128, compute_dtype=torch.float32)),
         "full_matrix_bf16_us": timed(full_matrix),
     }
-    # products per step: Gram (2 d^2 cols per block) and update (2 d^2 cols), d = 128, cols = 4096
-    out["per_head_TFLOPs_bf16"] = round(5 * 48 * 4 * 128 * 128 * 4096 / (out["per_head_bf16_us"] * 1e-6) / 1e12, 1)
+    # HBM bytes of the collapsed bf16 path: G read twice (Gram, apply) and Y written once, the fp32 Gram
+    # partials (48 blocks x 5 slices) written and read once, M (two bf16 terms) written and read once
+    nbytes = 3 * 48 * 128 * 4096 * 2 + 2 * 48 * 5 * 128 * 128 * 4 + 2 * 48 * 2 * 128 * 128 * 2
+    out["per_head_bf16_hbm_bytes"] = nbytes
+    out["per_head_bf16_GBps"] = round(nbytes / (out["per_head_bf16_us"] * 1e-6) / 1e9, 1)
     return out
 
 

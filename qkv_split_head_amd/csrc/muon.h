@@ -435,31 +435,41 @@ __global__ __launch_bounds__(kWave * (D / 32), 2) void ns_update_kernel(const ui
 // and the result is M G with M = M_steps scale / (n + eps): the same function of G as the steps
 // taken on X (ns_poly_kernel and the update), with two passes over G (its Gram matrix, then M G)
 // instead of two a step.  Every matrix here is a polynomial in A0, hence symmetric, which the
-// products use: product(a, b) takes tile (t, w) = rows 32 t + [0, 32) of a (A operand) against rows
-// 32 w + [0, 32) of b (B operand), a b^T, and lane (rr, h) of wave w reads it transposed, as row
-// r = 32 w + rr, columns c = 32 t + 8 e4 + 4 h + [0, 4) of b a^T, in registers 4 e4 + [0, 4) of tile t:
-// each wave then holds whole rows of every result, which is what its next uses need.
+// products use: product(a, b) takes tiles of a b^T, rows 32 t + [0, 32) of a (A operand) against a
+// wave's 32 rows of b (B operand), and reads them transposed, as rows of b a^T: each wave then holds
+// rows of every result, in the pieces that its LDS writes need.
 // Precision: every factor is held as two bf16 terms, hi = bf16(v) and lo = bf16(v - hi) (within
 // 2^-16 |v|), and every product is hi hi + hi lo + lo hi with fp32 accumulation (within about 2^-14
 // of |a| |b|); M goes out in the same two terms, applied as (hi + lo) G by ns_update_kernel<SPLIT>.
 // One bf16 rounding of M (2^-9 relative) would not do: M's entries grow with the block's condition
 // while M G stays near orthogonal, so its rounding errors do not cancel.
-// One workgroup per block (D / 32 waves, wave w owning rows 32 w + [0, 32) of every result).  LDS:
-// the current A'_k (or P_k A'_k) and P_k, each as hi and lo in gram_partials_kernel's layout (chunks
-// of 64 columns, row r's 16-byte piece j at j ^ ((r / 2) mod 8)); M stays in registers and reaches
-// the B operand through a swap between lanes rr and rr + 32.
+// One workgroup per block, ns_collapse_waves(D) waves: wave w owns rows 32 (w mod D/32) + [0, 32) and
+// its group of column tiles of every result.  LDS: two regions of a D x D matrix each as hi and lo, in
+// gram_partials_kernel's layout (chunks of 64 columns, row r's 16-byte piece j at j ^ ((r / 2) mod 8)):
+// rp holds P_k, ra holds A'_k, then P_k A'_k, then M_k while M_{k+1} is formed.
+// Waves of the collapse kernel: D / 32 row bands times up to QKVNR_NS_CSPLIT groups of column tiles, one
+// tile a wave by default (16 waves for D = 128, four a SIMD: 45 us for 48 blocks of 128, against 47 us with
+// two tiles a wave and 65 us with four).
+#ifndef QKVNR_NS_CSPLIT
+#define QKVNR_NS_CSPLIT 4
+#endif
+constexpr int ns_collapse_waves(int d) { return (d / 32) * (QKVNR_NS_CSPLIT < d / 32 ? QKVNR_NS_CSPLIT : d / 32); }
 template <int D>
-__global__ __launch_bounds__(kWave * (D / 32), 1) void ns_collapse_kernel(const float* __restrict__ gram, int parts,
-                                                                         int steps, float scale, float eps,
-                                                                         uint16_t* __restrict__ m) {
+__global__ __launch_bounds__(kWave * ns_collapse_waves(D), 1) void ns_collapse_kernel(const float* __restrict__ gram,
+                                                                                     int parts, int steps,
+                                                                                     float scale, float eps,
+                                                                                     uint16_t* __restrict__ m) {
   static_assert(D == 64 || D == 128, "block sides 64 and 128");
-  constexpr int T = D / 32, THREADS = kWave * T, N = D * D, V = N / 4 / THREADS, KS = D / 16;
-  __shared__ uint4 ra[2][N / 8];  // A'_k, then P_k A'_k: hi, lo
+  constexpr int T = D / 32, WAVES = ns_collapse_waves(D), TH = T * T / WAVES, THREADS = kWave * WAVES;
+  constexpr int N = D * D, V = N / 4 / THREADS;
+  constexpr int KS = D / 16;
+  __shared__ uint4 ra[2][N / 8];  // A'_k, then P_k A'_k, then M_k: hi, lo
   __shared__ uint4 rp[2][N / 8];  // P_k: hi, lo
-  __shared__ float tred[T];
+  __shared__ float tred[WAVES];
   const int lane = threadIdx.x & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
-  const int rr = lane % 32, h = lane / 32, sw = (rr >> 1) & 7, r = 32 * w + rr;
+  const int rr = lane % 32, h = lane / 32, sw = (rr >> 1) & 7;
+  const int r = 32 * (w % T) + rr, t0 = (w / T) * TH;  // this lane's row; this wave's first column tile
   const int64_t blk = blockIdx.x;
   auto lds_barrier = [] {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -491,29 +501,42 @@ __global__ __launch_bounds__(kWave * (D / 32), 1) void ns_collapse_kernel(const 
     unpack4(reinterpret_cast<const uint2*>(&reg[1][slot(row, col)])[(col >> 2) & 1], b);
     return make_float4(a[0] + b[0], a[1] + b[1], a[2] + b[2], a[3] + b[3]);
   };
-  auto split3 = [](f32x16_t acc, bf16x8_t ah, bf16x8_t al, bf16x8_t bh, bf16x8_t bl) {
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc, 0, 0, 0);
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc, 0, 0, 0);
-  };
-  // rows 32 t + [0, 32) of fa against rows r of fb, every tile t
-  auto product = [&](uint4 (*fa)[N / 8], uint4 (*fb)[N / 8], f32x16_t (&acc)[T]) {
+  // product(a, b): tiles t0 + i of a b^T (rows 32 t of a against rows of b in this wave's band), each read
+  // transposed: acc[i] register 4 e4 + j is (b a^T)[r][32 (t0 + i) + 8 e4 + 4 h + j].  Every operand is
+  // hi + lo; hi hi + hi lo + lo hi, fp32 accumulation.
+  auto product = [&](uint4 (*fa)[N / 8], uint4 (*fb)[N / 8], f32x16_t (&acc)[TH]) {
 #pragma unroll
-    for (int t = 0; t < T; ++t) acc[t] = f32x16_t{};
+    for (int i = 0; i < TH; ++i) acc[i] = f32x16_t{};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const int base = (s / 4) * D * 8, pos = (2 * (s % 4) + h) ^ sw;
       const bf16x8_t bh = __builtin_bit_cast(bf16x8_t, fb[0][base + r * 8 + pos]);
       const bf16x8_t bl = __builtin_bit_cast(bf16x8_t, fb[1][base + r * 8 + pos]);
 #pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const int ra_ = base + (32 * t + rr) * 8 + pos;
-        acc[t] = split3(acc[t], __builtin_bit_cast(bf16x8_t, fa[0][ra_]), __builtin_bit_cast(bf16x8_t, fa[1][ra_]),
-                        bh, bl);
+      for (int i = 0; i < TH; ++i) {
+        const int ia = base + (32 * (t0 + i) + rr) * 8 + pos;
+        const bf16x8_t ah = __builtin_bit_cast(bf16x8_t, fa[0][ia]);
+        const bf16x8_t al = __builtin_bit_cast(bf16x8_t, fa[1][ia]);
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc[i], 0, 0, 0);
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc[i], 0, 0, 0);
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc[i], 0, 0, 0);
       }
     }
   };
+  auto col_of = [&](int i, int e4) { return 32 * (t0 + i) + 8 * e4 + 4 * h; };
   auto tile4 = [](const f32x16_t& a, int e4) { return make_float4(a[4 * e4], a[4 * e4 + 1], a[4 * e4 + 2], a[4 * e4 + 3]); };
+  auto put_all = [&](uint4 (*reg)[N / 8], const float4 (&v)[TH][4]) {
+#pragma unroll
+    for (int i = 0; i < TH; ++i)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) put(reg, r, col_of(i, e4), v[i][e4]);
+  };
+  auto regs = [&](const f32x16_t (&acc)[TH], float4 (&v)[TH][4]) {
+#pragma unroll
+    for (int i = 0; i < TH; ++i)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) v[i][e4] = tile4(acc[i], e4);
+  };
 
   // A0 = ((g0 + g1) + g2) + ...: thread x sums the 4 values at 4 (j THREADS + x), two slices in flight
   const float* g = gram + blk * parts * N;
@@ -558,7 +581,7 @@ __global__ __launch_bounds__(kWave * (D / 32), 1) void ns_collapse_kernel(const 
   __syncthreads();
   float n2 = 0.0f;
 #pragma unroll
-  for (int i = 0; i < T; ++i) n2 += tred[i];
+  for (int i = 0; i < WAVES; ++i) n2 += tred[i];
   const float norm_inv = 1.0f / (sqrtf(n2) + eps), a2s = norm_inv * norm_inv;
 #pragma unroll
   for (int j = 0; j < V; ++j) {
@@ -567,18 +590,18 @@ __global__ __launch_bounds__(kWave * (D / 32), 1) void ns_collapse_kernel(const 
   }
   lds_barrier();
 
-  float4 mr[T][4];  // row r of M: columns 32 t + 8 e4 + 4 h + [0, 4)
-  f32x16_t acc[T];
+  float4 mr[TH][4];  // M_k: row r, this wave's columns
+  f32x16_t acc[TH];
   for (int k = 0; k < steps; ++k) {
     // P_k = 3.4445 I - 4.7750 A' + 2.0315 A' A'
     product(ra, ra, acc);
-    float4 pr[T][4];
+    float4 pr[TH][4];
 #pragma unroll
-    for (int t = 0; t < T; ++t)
+    for (int i = 0; i < TH; ++i)
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
-        const int c = 32 * t + 8 * e4 + 4 * h;
-        const float4 a1 = get(ra, r, c), a2 = tile4(acc[t], e4);
+        const int c = col_of(i, e4);
+        const float4 a1 = get(ra, r, c), a2 = tile4(acc[i], e4);
         float4 pv = make_float4(fmaf(kNsC, a2.x, kNsB * a1.x), fmaf(kNsC, a2.y, kNsB * a1.y),
                                 fmaf(kNsC, a2.z, kNsB * a1.z), fmaf(kNsC, a2.w, kNsB * a1.w));
         const int dd = r - c;  // the diagonal element of this row, if among these 4 columns
@@ -586,78 +609,50 @@ __global__ __launch_bounds__(kWave * (D / 32), 1) void ns_collapse_kernel(const 
         if (dd == 1) pv.y += kNsA;
         if (dd == 2) pv.z += kNsA;
         if (dd == 3) pv.w += kNsA;
-        pr[t][e4] = pv;
-        put(rp, r, c, pv);
+        pr[i][e4] = pv;
       }
+    put_all(rp, pr);
     lds_barrier();
-    if (k == 0) {
-#pragma unroll
-      for (int t = 0; t < T; ++t)
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) mr[t][e4] = pr[t][e4];
-    } else {  // M = P_k M: rows of P (LDS) against rows r of M (registers)
-      // B operand of k-step s: row r, columns 16 s + 8 h + [0, 8), i.e. piece 2 s + h, of which this lane
-      // holds half h; the other half comes from lane rr + 32 (h ^ 1), which sends its half of that piece
-#pragma unroll
-      for (int t = 0; t < T; ++t) acc[t] = f32x16_t{};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const float4 e = mr[s / 2][2 * (s % 2)], o = mr[s / 2][2 * (s % 2) + 1];  // pieces 2 s and 2 s + 1
-        const float4 own = h ? o : e, send = h ? e : o;
-        const float4 got = make_float4(__shfl_xor(send.x, 32, kWave), __shfl_xor(send.y, 32, kWave),
-                                       __shfl_xor(send.z, 32, kWave), __shfl_xor(send.w, 32, kWave));
-        const float4 lo4 = h ? got : own, hi4 = h ? own : got;  // columns 8 (2 s + h) + [0, 4) and + [4, 8)
-        const float v[8] = {lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
-        uint32_t bh[4], bl[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          bh[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
-          bl[i] = pack_bf16x2(rest(v[2 * i], bh[i], 0), rest(v[2 * i + 1], bh[i], 1));
-        }
-        const bf16x8_t bhv = __builtin_bit_cast(bf16x8_t, make_uint4(bh[0], bh[1], bh[2], bh[3]));
-        const bf16x8_t blv = __builtin_bit_cast(bf16x8_t, make_uint4(bl[0], bl[1], bl[2], bl[3]));
-        const int base = (s / 4) * D * 8, pos = (2 * (s % 4) + h) ^ sw;
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-          const int ia = base + (32 * t + rr) * 8 + pos;
-          acc[t] = split3(acc[t], __builtin_bit_cast(bf16x8_t, rp[0][ia]), __builtin_bit_cast(bf16x8_t, rp[1][ia]),
-                          bhv, blv);
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < T; ++t)
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) mr[t][e4] = tile4(acc[t], e4);
-    }
+    float4 an[TH][4];
     if (k + 1 < steps) {
       // A'_{k+1} = (P_k A'_k) P_k.  The transposed reading makes product(a, b) = b a^T, so the factors go in
       // this order: another one (P_k P_k A'_k, say) is as good in exact arithmetic but not symmetric in
       // form, and its rounding's antisymmetric part would grow from step to step
       product(ra, rp, acc);  // P_k A'_k
       lds_barrier();         // every read of A'_k is done
-#pragma unroll
-      for (int t = 0; t < T; ++t)
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) put(ra, r, 32 * t + 8 * e4 + 4 * h, tile4(acc[t], e4));
+      regs(acc, an);
+      put_all(ra, an);
       lds_barrier();
       product(rp, ra, acc);  // (P_k A'_k) P_k
-      lds_barrier();  // every read of P_k A'_k is done
+      regs(acc, an);
+      lds_barrier();         // every read of P_k A'_k is done
+    }
+    if (k == 0) {
 #pragma unroll
-      for (int t = 0; t < T; ++t)
+      for (int i = 0; i < TH; ++i)
 #pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) put(ra, r, 32 * t + 8 * e4 + 4 * h, tile4(acc[t], e4));
+        for (int e4 = 0; e4 < 4; ++e4) mr[i][e4] = pr[i][e4];
+    } else {  // M_{k+1} = M_k P_k (= P_k M_k): rows of P against rows of M_k, staged in ra
+      put_all(ra, mr);
+      lds_barrier();
+      product(rp, ra, acc);
+      regs(acc, mr);
+      lds_barrier();  // every read of M_k (and of P_k) is done
+    }
+    if (k + 1 < steps) {
+      put_all(ra, an);
       lds_barrier();
     }
   }
-  // M scale / (n + eps) as hi and lo: m + b 2 D D (hi) and + D D (lo), 8 bytes of each per (t, e4)
+  // M scale / (n + eps) as hi and lo: m + b 2 D D (hi) and + D D (lo), 8 bytes of each per (tile, e4)
   const float ms = scale * norm_inv;
   uint16_t* mh = m + blk * 2 * N + r * D;
 #pragma unroll
-  for (int t = 0; t < T; ++t)
+  for (int i = 0; i < TH; ++i)
 #pragma unroll
     for (int e4 = 0; e4 < 4; ++e4) {
-      const int c = 32 * t + 8 * e4 + 4 * h;
-      const float v[4] = {mr[t][e4].x * ms, mr[t][e4].y * ms, mr[t][e4].z * ms, mr[t][e4].w * ms};
+      const int c = col_of(i, e4);
+      const float v[4] = {mr[i][e4].x * ms, mr[i][e4].y * ms, mr[i][e4].z * ms, mr[i][e4].w * ms};
       const uint2 hi = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
       const uint2 lo = make_uint2(pack_bf16x2(rest(v[0], hi.x, 0), rest(v[1], hi.x, 1)),
                                   pack_bf16x2(rest(v[2], hi.y, 0), rest(v[3], hi.y, 1)));

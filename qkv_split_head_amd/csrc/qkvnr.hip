@@ -754,9 +754,11 @@ int qkvnr_ns_collapse(int64_t blocks, int32_t d, const float* gram, int32_t part
   auto* mo = static_cast<uint16_t*>(m);
   const dim3 grid(static_cast<uint32_t>(blocks));
   if (d == 128)
-    hipLaunchKernelGGL((ns_collapse_kernel<128>), grid, dim3(kWave * 4), 0, stream, gram, parts, steps, scale, eps, mo);
+    hipLaunchKernelGGL((ns_collapse_kernel<128>), grid, dim3(kWave * ns_collapse_waves(128)), 0, stream, gram, parts,
+                       steps, scale, eps, mo);
   else
-    hipLaunchKernelGGL((ns_collapse_kernel<64>), grid, dim3(kWave * 2), 0, stream, gram, parts, steps, scale, eps, mo);
+    hipLaunchKernelGGL((ns_collapse_kernel<64>), grid, dim3(kWave * ns_collapse_waves(64)), 0, stream, gram, parts,
+                       steps, scale, eps, mo);
   return launched("Newton-Schulz collapse");
 }
 
