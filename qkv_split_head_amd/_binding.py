@@ -482,6 +482,12 @@ def proj_forward(x: torch.Tensor, w_qkv: torch.Tensor, positions: Optional[torch
     x [T, hidden] and w_qkv [(n_q + 2 n_kv) * head_dim, hidden] are contiguous;
     the weight's head blocks are in the ``kind`` order.  Returns contiguous
     (q [T, n_q, D], k [T, n_kv, D], v [T, n_kv, D]).
+
+    The packed product is never rounded, so q, k and v differ from a library
+    GEMM followed by ``forward`` by at most a rounding.  It is not the faster
+    route on MI355X: at 16384 x 4096 -> 6144 it takes about 700 us against
+    about 594 us for ``torch.matmul`` then ``forward``, whose GEMM alone takes
+    about 526 us.
     """
     if x.dim() != 2 or w_qkv.dim() != 2 or not x.is_contiguous() or not w_qkv.is_contiguous():
         raise ValueError("x and w_qkv must be contiguous 2-D tensors")
