@@ -83,6 +83,36 @@ def test_rank_deficient_blocks_through_the_collapsed_path():
     assert nerr <= 2.0 ** -5
 
 
+@pytest.mark.parametrize("D,cols,steps", [(128, 1024, 1), (128, 1024, 3), (64, 512, 7), (32, 256, 3)])
+def test_other_step_counts_match_the_oracle(D, cols, steps):
+    rng = np.random.default_rng(D + cols + steps)
+    n_q, n_kv = 4, 2
+    g = torch.from_numpy(rng.standard_normal(((n_q + 2 * n_kv) * D, cols)).astype(np.float32)).cuda()
+    g = g.to(torch.bfloat16)
+    got = per_head_newton_schulz(g, n_q, n_kv, D, steps=steps).float().cpu().numpy()
+    ref = oracle_muon.per_head_update(g.float().cpu().numpy().astype(np.float64), n_q, n_kv, D, steps=steps)
+    nerr = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    print(f"[muon] blocks of {D} x {cols}, {steps} steps: Frobenius-relative {nerr:.2e}", flush=True)
+    assert nerr <= (2.0 ** -6 if D in (64, 128) else 2.0 ** -5)
+
+
+@pytest.mark.parametrize("D,dtype", [(128, torch.bfloat16), (32, torch.bfloat16), (128, torch.float32)])
+def test_an_all_zero_head_block_stays_zero(D, dtype):
+    # ||G||_F = 0 for that block: the first step divides by eps, the block stays exactly zero (no NaN), and the
+    # other blocks are updated as they would be alone
+    rng = np.random.default_rng(D)
+    n_q, n_kv, cols = 2, 1, 512
+    w = rng.standard_normal(((n_q + 2 * n_kv) * D, cols)).astype(np.float32)
+    w[D:2 * D] = 0.0
+    g = torch.from_numpy(w).cuda().to(dtype)
+    got = per_head_newton_schulz(g, n_q, n_kv, D).float().cpu().numpy()
+    assert np.all(got[D:2 * D] == 0.0) and np.all(np.isfinite(got))
+    ref = oracle_muon.per_head_update(g.float().cpu().numpy().astype(np.float64), n_q, n_kv, D)
+    assert np.all(ref[D:2 * D] == 0.0)
+    nerr = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    assert nerr <= (1e-4 if dtype == torch.float32 else 2.0 ** -5)
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_sectioned_and_interleaved_give_the_same_blocks_bitwise(dtype):
     rng = np.random.default_rng(9)
