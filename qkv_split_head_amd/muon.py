@@ -56,8 +56,6 @@ def _newton_schulz_blocks(X: torch.Tensor, scale: float, steps: int, eps: float)
     parts = _gram_parts(nb, cols) if own_gram else 1
     gram = torch.empty((nb, parts, d, d), dtype=torch.float32, device=X.device)
     if own_gram and d in (64, 128):
-        if steps == 0:
-            return X
         # collapsed: G's Gram matrices, the whole iteration as M per block, then M G
         b.qkvnr_gram_partials(nb, d, cols, X, parts, gram)
         M = torch.empty((nb, 2, d, d), dtype=X.dtype, device=X.device)
@@ -85,6 +83,8 @@ def per_head_newton_schulz(G: torch.Tensor, n_q: int, n_kv: int, head_dim: int, 
     Each block is scaled by max(1, head_dim / in_features) ** 0.5.  Every sum is
     taken in a fixed order: the result does not change from run to run.
     """
+    if steps < 1:   # the first step carries the Frobenius normalisation
+        raise ValueError(f"steps must be >= 1, got {steps}")
     if G.dim() != 2:
         raise ValueError("G must be a 2-D weight")
     b._need(G, "G", contiguous=False)   # the kernels take device addresses: a host weight is refused here

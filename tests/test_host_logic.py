@@ -8,6 +8,7 @@
   table row, negative position) must be refused by the staged path too.
 - ``_keep_workspace_clean``: a backward call that fails after kernels may have
   been enqueued drops the module's cached workspace of that device.
+- ``per_head_newton_schulz`` refuses zero steps before touching the device.
 """
 import numpy as np
 import pytest
@@ -91,3 +92,10 @@ def test_validation_error_keeps_the_cached_workspace():
     finally:
         bnd._workspaces.pop(7, None)
 
+
+
+def test_newton_schulz_refuses_zero_steps():
+    # every path folds the Frobenius normalisation into the first step, so no step is refused before any device work
+    from qkv_split_head_amd.muon import per_head_newton_schulz
+    with pytest.raises(ValueError, match="steps"):
+        per_head_newton_schulz(torch.zeros((3 * 64, 128)), 1, 1, 64, steps=0)
