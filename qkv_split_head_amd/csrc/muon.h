@@ -1,4 +1,4 @@
-// Per-head Newton-Schulz on fused QKV weights: the per-block steps.
+// Per-head Newton-Schulz on fused QKV weights: the per-block steps, and the steps collapsed.
 //
 // DeepSpeed page "[muon] Per-head Newton-Schulz for fused QKV projections",
 // "What this PR does": a fused q|k|v weight is a stack of head blocks of
@@ -13,8 +13,12 @@
 // the long side), as partial sums over column slices; ns_poly_kernel adds the
 // partials as it loads them and forms P, folding in the first step's
 // normalisation (||G||_F^2 is the trace of G G^T: A is divided by its square
-// and P by the norm) and the last step's scale; the update P X is a plain
-// batched GEMM.
+// and P by the norm) and the last step's scale; the update P X is
+// ns_update_kernel (bf16 blocks of side 64 and 128) or a batched GEMM.
+//
+// For bf16 blocks of side 64 and 128 the steps are also collapsed into one d x d
+// matrix M per block (ns_collapse_kernel, from the Gram partials of G), and the
+// result is M G in one more pass (ns_update_kernel<SPLIT>).
 #pragma once
 
 #include "device.h"
@@ -447,6 +451,7 @@ __global__ __launch_bounds__(kWave * (D / 32), 2) void ns_update_kernel(const ui
 // its group of column tiles of every result.  LDS: two regions of a D x D matrix each as hi and lo, in
 // gram_partials_kernel's layout (chunks of 64 columns, row r's 16-byte piece j at j ^ ((r / 2) mod 8)):
 // rp holds P_k, ra holds A'_k, then P_k A'_k, then M_k while M_{k+1} is formed.
+//
 // Waves of the collapse kernel: D / 32 row bands times up to QKVNR_NS_CSPLIT groups of column tiles, one
 // tile a wave by default (16 waves for D = 128, four a SIMD: 45 us for 48 blocks of 128, against 47 us with
 // two tiles a wave and 65 us with four).
