@@ -103,7 +103,7 @@ struct GqaArgs {
   int32_t n_q;
   int32_t heads;        // head blocks per token
   int32_t iters;        // wave iterations per token
-  uint32_t grp_magic;   // ceil(2^32 / (q_per_kv + 2)), exact division for head < 2^16
+  uint32_t q_magic;     // ceil(2^32 / q_per_kv), exact division for head < 2^16
   // paged store
   const int32_t* bt;
   int32_t bt_stride;
@@ -114,16 +114,30 @@ struct GqaArgs {
   double turns[kMaxPairs];
 };
 
-// Which output head a packed head block is: type 0 = q, 1 = k, 2 = v, and its index.
+// Heads are taken kind-major in both layouts: head h < n_q is q head h, then come the n_kv k heads and the
+// n_kv v heads.  So every iteration of HPI heads is one kind when n_q and n_kv are multiples of HPI (the
+// interleaved Muse layout as much as the sectioned one), and iter_kind's uniform bodies apply.
+// type 0 = q, 1 = k, 2 = v, and the head's index in its output.
 __device__ __forceinline__ void map_head(const GqaArgs& a, int h, int& type, int& idx) {
-  if (a.kind == kInterleaved) {
-    const int g = static_cast<int>(__umulhi(static_cast<uint32_t>(h), a.grp_magic));
-    const int s = h - g * (a.q_per_kv + 2);
-    type = s < a.q_per_kv ? 0 : (s == a.q_per_kv ? 1 : 2);
-    idx = type == 0 ? g * a.q_per_kv + s : g;
+  type = h < a.n_q ? 0 : (h < a.n_q + a.n_kv ? 1 : 2);
+  idx = h - (type == 0 ? 0 : (type == 1 ? a.n_q : a.n_q + a.n_kv));
+}
+
+// Where head h sits in the packed row, in head blocks: h itself in the sectioned layout; in the interleaved
+// one q head g Q + s is block g (Q + 2) + s, and the k and v heads of group g are blocks g (Q + 2) + Q and
+// g (Q + 2) + Q + 1.  An iteration's blocks are then not one span of the row (HPI q heads span 1 + HPI / Q
+// groups, HPI k heads sit one group apart), but each block is whole 128-byte lines.
+template <bool ILV>
+__device__ __forceinline__ int mem_head(const GqaArgs& a, int h) {
+  if constexpr (!ILV) {
+    return h;
   } else {
-    type = h < a.n_q ? 0 : (h < a.n_q + a.n_kv ? 1 : 2);
-    idx = h - (type == 0 ? 0 : (type == 1 ? a.n_q : a.n_q + a.n_kv));
+    const int Q = a.q_per_kv;
+    if (h < a.n_q) {
+      const int g = static_cast<int>(__umulhi(static_cast<uint32_t>(h), a.q_magic));
+      return g * (Q + 2) + (h - g * Q);
+    }
+    return h < a.n_q + a.n_kv ? (h - a.n_q) * (Q + 2) + Q : (h - a.n_q - a.n_kv) * (Q + 2) + Q + 1;
   }
 }
 
@@ -238,7 +252,7 @@ __device__ __forceinline__ void fwd_iter(int kind, const uint4& xb, const uint4&
 // U iterations per work unit, DEPTH of their loads in flight at once: (kFwdU,
 // kFwdDepth) for streaming batches, (1, 1) for small batches, where the
 // shortest per-wave chain (one load, one store) gives the lowest latency.
-template <typename IO, int D, bool ROPE, bool PAGED, int U, int DEPTH>
+template <typename IO, int D, bool ROPE, bool PAGED, int U, int DEPTH, bool ILV>
 __global__ __launch_bounds__(kBlockThreads) void fwd_gqa_kernel(const GqaArgs a) {
   static_assert(DEPTH >= 1 && DEPTH <= U, "load depth must be in [1, units]");
   using G = Geo<IO, D>;
@@ -273,7 +287,7 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_gqa_kernel(const GqaArgs a)
   uint4 buf[U];
 #pragma unroll
   for (int j = 0; j < DEPTH; ++j)
-    buf[j] = ld_stream(row + min((it0 + j) * HPI + hs, a.heads - 1) * HB + cb);
+    buf[j] = ld_stream(row + mem_head<ILV>(a, min((it0 + j) * HPI + hs, a.heads - 1)) * HB + cb);
   __builtin_amdgcn_sched_barrier(0);
 
   float cs[EPC], sn[EPC];
@@ -289,7 +303,7 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_gqa_kernel(const GqaArgs a)
                           type, idx, cb, a.q, a.k, a.v, t, kv_tok, a.n_q, a.n_kv);
     if (j + DEPTH < U) {
       __builtin_amdgcn_sched_barrier(0);
-      buf[j + DEPTH] = ld_stream(row + min((it0 + j + DEPTH) * HPI + hs, a.heads - 1) * HB + cb);
+      buf[j + DEPTH] = ld_stream(row + mem_head<ILV>(a, min((it0 + j + DEPTH) * HPI + hs, a.heads - 1)) * HB + cb);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -310,7 +324,7 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_gqa_kernel(const GqaArgs a)
 // the last head, and a v head, whose input is not needed, reads the q weight
 // chunk (cached) in place of its input chunk: no load is skipped, because a
 // skipped load would turn every later wait into a full drain.
-template <int HB>
+template <int HB, bool ILV>
 // (`a` by value: with a reference to the kernel argument block the compiler
 // copies the whole block to scratch.)
 __device__ __forceinline__ void bwd_load(const GqaArgs a, int64_t t, int h, const uint8_t* row, int cb,
@@ -321,7 +335,7 @@ __device__ __forceinline__ void bwd_load(const GqaArgs a, int64_t t, int h, cons
   const uint8_t* g = type == 0 ? a.dq + (t * a.n_q + idx) * HB
                                : (type == 1 ? a.dk : a.dv) + (t * a.n_kv + idx) * HB;
   gb = ld_stream(g + cb);
-  xb = ld_stream(type != 2 ? row + h * HB + cb : a.wq + cb);
+  xb = ld_stream(type != 2 ? row + mem_head<ILV>(a, h) * HB + cb : a.wq + cb);
 }
 
 // One backward iteration of the lane's head h (type from map_head; kind from
@@ -395,7 +409,7 @@ __device__ __forceinline__ void bwd_iter(int kind, const uint4& xb, const uint4&
   }
 }
 
-template <typename IO, int D, bool ROPE>
+template <typename IO, int D, bool ROPE, bool ILV>
 __global__ __launch_bounds__(kBwdBlockThreads) void bwd_gqa_kernel(const GqaArgs a) {
   using G = Geo<IO, D>;
   constexpr int EPC = G::EPC, LPH = G::LPH, HPI = G::HPI, HB = G::HB, U = kBwdU;
@@ -428,7 +442,7 @@ __global__ __launch_bounds__(kBwdBlockThreads) void bwd_gqa_kernel(const GqaArgs
     // kBwdDepth iterations' loads go out at once; each store is followed by
     // the loads of the next iteration
 #pragma unroll
-    for (int j = 0; j < kBwdDepth; ++j) bwd_load<HB>(a, t, (it0 + j) * HPI + hs, row, cb, xb[j], gb[j]);
+    for (int j = 0; j < kBwdDepth; ++j) bwd_load<HB, ILV>(a, t, (it0 + j) * HPI + hs, row, cb, xb[j], gb[j]);
     __builtin_amdgcn_sched_barrier(0);
     float cs[EPC], sn[EPC];
     if constexpr (ROPE) unit_cos_sin<EPC, LPH>(p, tpp, c, cs, sn);
@@ -440,11 +454,15 @@ __global__ __launch_bounds__(kBwdBlockThreads) void bwd_gqa_kernel(const GqaArgs
       const int h = (it0 + j) * HPI + hs;
       int type, idx;
       map_head(a, h, type, idx);
+      // bwd_iter stores head h at drow + h HB: in the interleaved layout the row pointer is shifted so that
+      // this lands on the head's block (the sectioned layout passes the row itself)
+      uint8_t* dr = drow;
+      if constexpr (ILV) dr += static_cast<int64_t>(mem_head<ILV>(a, h) - h) * HB;
       bwd_iter<IO, D, ROPE>(iter_kind(h, a.heads, type), xb[j], gb[j], wq_raw, wk_raw, cs, sn, a.eps, a.inv_d, h,
-                            a.heads, type, drow, cb, accq, acck);
+                            a.heads, type, dr, cb, accq, acck);
       if (j + kBwdDepth < U) {
         __builtin_amdgcn_sched_barrier(0);
-        bwd_load<HB>(a, t, (it0 + j + kBwdDepth) * HPI + hs, row, cb, xb[j + kBwdDepth], gb[j + kBwdDepth]);
+        bwd_load<HB, ILV>(a, t, (it0 + j + kBwdDepth) * HPI + hs, row, cb, xb[j + kBwdDepth], gb[j + kBwdDepth]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }

@@ -212,8 +212,8 @@ void plan_gqa(GqaArgs& a, const qkvnr_layout* L, int U, double theta) {
   a.upt_magic = a.upt == 1 ? 0ull
                            : static_cast<uint64_t>(((static_cast<unsigned __int128>(1) << 64) + a.upt - 1) /
                                                    static_cast<unsigned __int128>(a.upt));
-  const uint32_t d = static_cast<uint32_t>(a.q_per_kv + 2);
-  a.grp_magic = static_cast<uint32_t>((0x100000000ull + d - 1) / d);
+  const uint32_t d = static_cast<uint32_t>(a.q_per_kv);
+  a.q_magic = static_cast<uint32_t>((0x100000000ull + d - 1) / d);
   a.row_bytes = L->in_row_stride * elem_bytes(L->dtype);
   a.inv_d = 1.0f / static_cast<float>(L->head_dim);
   fill_turns(a.turns, theta, L->rope_dim);
@@ -251,12 +251,28 @@ int launch_pieces(int64_t items, int per_block, const char* what, SetFirst&& set
 // part), a batch is latency-bound: the forward then uses one iteration per wave.
 constexpr int64_t kSmallBatchUnits = 2048;
 
+// One forward launch, the layout a template argument (the interleaved one maps heads to row blocks).
+template <typename IO, int DD, bool R, bool PAGED, int U, int DEPTH>
+void fwd_gqa_launch(const GqaArgs& a, dim3 g, dim3 b, hipStream_t s) {
+  if (a.kind == kInterleaved)
+    hipLaunchKernelGGL((fwd_gqa_kernel<IO, DD, R, PAGED, U, DEPTH, true>), g, b, QKVNR_FWD_LDS, s, a);
+  else
+    hipLaunchKernelGGL((fwd_gqa_kernel<IO, DD, R, PAGED, U, DEPTH, false>), g, b, QKVNR_FWD_LDS, s, a);
+}
+
+template <typename IO, int DD, bool R>
+void bwd_gqa_launch(const GqaArgs& a, dim3 g, dim3 b, hipStream_t s) {
+  if (a.kind == kInterleaved)
+    hipLaunchKernelGGL((bwd_gqa_kernel<IO, DD, R, true>), g, b, QKVNR_BWD_LDS, s, a);
+  else
+    hipLaunchKernelGGL((bwd_gqa_kernel<IO, DD, R, false>), g, b, QKVNR_BWD_LDS, s, a);
+}
+
 template <bool PAGED, int U, int DEPTH>
 int launch_fwd_gqa(GqaArgs a, int32_t dtype, int32_t D, bool rope, hipStream_t s) {
   const dim3 b(kBlockThreads);
   auto launch = [&](dim3 g) {
-#define QKVNR_FWD(IO, DD, R) \
-  hipLaunchKernelGGL((fwd_gqa_kernel<IO, DD, R, PAGED, U, DEPTH>), g, b, QKVNR_FWD_LDS, s, a)
+#define QKVNR_FWD(IO, DD, R) fwd_gqa_launch<IO, DD, R, PAGED, U, DEPTH>(a, g, b, s)
     if (dtype == QKVNR_BF16) {
       if (D == 64) { if (rope) QKVNR_FWD(uint16_t, 64, true); else QKVNR_FWD(uint16_t, 64, false); }
       else         { if (rope) QKVNR_FWD(uint16_t, 128, true); else QKVNR_FWD(uint16_t, 128, false); }
@@ -272,7 +288,7 @@ int launch_fwd_gqa(GqaArgs a, int32_t dtype, int32_t D, bool rope, hipStream_t s
 int launch_bwd_gqa(GqaArgs a, int32_t dtype, int32_t D, bool rope, hipStream_t s, bool* enqueued) {
   const dim3 b(kBwdBlockThreads);
   auto launch = [&](dim3 g) {
-#define QKVNR_BWD(IO, DD, R) hipLaunchKernelGGL((bwd_gqa_kernel<IO, DD, R>), g, b, QKVNR_BWD_LDS, s, a)
+#define QKVNR_BWD(IO, DD, R) bwd_gqa_launch<IO, DD, R>(a, g, b, s)
     if (dtype == QKVNR_BF16) {
       if (D == 64) { if (rope) QKVNR_BWD(uint16_t, 64, true); else QKVNR_BWD(uint16_t, 64, false); }
       else         { if (rope) QKVNR_BWD(uint16_t, 128, true); else QKVNR_BWD(uint16_t, 128, false); }
