@@ -267,7 +267,7 @@ __global__ __launch_bounds__(kNsThreads) void ns_poly_kernel(const float* __rest
 // D / 32 waves, chunks of 64 columns:
 // - X's chunk is loaded into registers three chunks ahead, thread (rg, cg) holding rows
 //   4 rg + [0, 4) of columns 8 cg + [0, 8), and written to LDS transposed (X^T, rows of D values
-//   along k): column n's 4 values go to piece k / 8 of row n at position (k / 8) ^ (n mod D/8);
+//   along k): column n's 4 values go to piece k / 8 of row n at position (k / 8) ^ xswz(n);
 // - the product is taken as Y^T = X^T P^T: the A operand is a row of X^T and the B operand a row
 //   of P, so P needs no transpose, and each lane keeps its P operands in registers for the whole
 //   slice.  Wave w forms rows 32 w + [0, 32) of Y for the chunk's 64 columns;
@@ -296,6 +296,14 @@ __global__ __launch_bounds__(kWave * (D / 32), 2) void ns_update_kernel(const ui
   static_assert(THREADS == 2 * D, "one thread per 4 x 8 patch of a chunk");
   __shared__ uint4 xt[2][kGramChunk * XP];
   __shared__ uint4 ys[2][D * YP];
+  // X^T row n's piece q sits at q ^ xswz(n).  A write instruction covers columns n = 8 cg + c (c fixed) of
+  // 8 consecutive k rows: for D = 128 the swizzle mixes n's bits 4-5 into bits 1-2 as well as taking n mod 16,
+  // so those lanes hit 32 bank pairs twice each (n mod 16 alone takes 2 values there: 4 lanes a pair); each
+  // 16 lanes of an operand read (16 consecutive n) still hit 16 different pieces.
+  auto xswz = [](int n) {
+    if constexpr (XP == 16) return (n & 15) ^ (((n >> 4) & 3) << 1);
+    else return n & (XP - 1);
+  };
   const int lane = threadIdx.x & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
   const int64_t blk = blockIdx.x;
@@ -329,8 +337,8 @@ __global__ __launch_bounds__(kWave * (D / 32), 2) void ns_update_kernel(const ui
       const uint2 lo = make_uint2((a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16));
       const uint2 hi = make_uint2((a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u));
       const int n0 = 8 * cg + 2 * d, n1 = n0 + 1;
-      reinterpret_cast<uint2*>(&buf[n0 * XP + ((k >> 3) ^ (n0 & (XP - 1)))])[(k >> 2) & 1] = lo;
-      reinterpret_cast<uint2*>(&buf[n1 * XP + ((k >> 3) ^ (n1 & (XP - 1)))])[(k >> 2) & 1] = hi;
+      reinterpret_cast<uint2*>(&buf[n0 * XP + ((k >> 3) ^ xswz(n0))])[(k >> 2) & 1] = lo;
+      reinterpret_cast<uint2*>(&buf[n1 * XP + ((k >> 3) ^ xswz(n1))])[(k >> 2) & 1] = hi;
     }
   };
   auto lds_barrier = [] {
@@ -351,7 +359,7 @@ __global__ __launch_bounds__(kWave * (D / 32), 2) void ns_update_kernel(const ui
 #pragma unroll
       for (int ni = 0; ni < 2; ++ni) {
         const int n = 32 * ni + rr;
-        const uint4 af = xb[n * XP + ((2 * s + h) ^ (n & (XP - 1)))];
+        const uint4 af = xb[n * XP + ((2 * s + h) ^ xswz(n))];
         if constexpr (SPLIT)
           ya[ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af),
                                                            __builtin_bit_cast(bf16x8_t, pl[s]), ya[ni], 0, 0, 0);
