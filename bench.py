@@ -597,51 +597,27 @@ def main():
     # ------------------------------------------------------------ decode, HIP-graph replays
     CALLS = 32  # forward calls per graph in the latency-bound legs
     if "decode" in legs:
-            # one graph holds CALLS forward calls (as a decode step holds every layer's), so the
+        # one graph holds CALLS forward calls (as a decode step holds every layer's), so the
         # per-call figure is GPU time plus the in-graph launch gap, not host submission
-            for Td in (1, 8, 64, 256):
-                dw = decode_interleaved(Td)
-                dq_ = dev_bf16(dw.qkv)
-                dp = torch.from_numpy(dw.positions).to(dev)
-                dwq_, dwk_ = dev_bf16(dw.q_norm_w), dev_bf16(dw.k_norm_w)
-                o = (torch.empty((Td, 128, 64), dtype=torch.bfloat16, device=dev),
-                     torch.empty((Td, 16, 64), dtype=torch.bfloat16, device=dev),
-                     torch.empty((Td, 16, 64), dtype=torch.bfloat16, device=dev))
-                dk_ = dict(kind="interleaved", n_kv=16, q_per_kv=8, head_dim=64, eps=1e-6, theta=5e5)
-                side = torch.cuda.Stream()
-                side.wait_stream(stream)
-                with torch.cuda.stream(side):
-                    for _ in range(3):
-                        qk.forward(dq_, dp, dwq_, dwk_, out=o, **dk_)
-                stream.wait_stream(side)
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g):
-                    for _ in range(CALLS):
-                        qk.forward(dq_, dp, dwq_, dwk_, out=o, **dk_)
-                for _ in range(5):
-                    g.replay()
-                n = 20
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                for _ in range(n):
-                    g.replay()
-                e1.record(stream)
-                torch.cuda.synchronize()
-                extras[f"decode_T{Td}_us"] = round(e0.elapsed_time(e1) / (n * CALLS) * 1e3, 2)
-                del g
-
-    # ------------------------------------------------------------ MLA latent rows into the paged pool
-    if "mla" in legs:
-            lw = latent_paged()
-            rows, lp, lwk = dev_bf16(lw.qkv), torch.from_numpy(lw.positions).to(dev), dev_bf16(lw.k_norm_w)
-            bt = torch.from_numpy(lw.block_table).to(dev)
-            pool = torch.zeros((lw.num_pages, lw.page_size, 576), dtype=torch.bfloat16, device=dev)
-            for _ in range(3):
-                qk.forward_latent_paged(rows, lp, lwk, bt, pool, tokens_per_req=lw.tokens_per_req)
+        for Td in (1, 8, 64, 256):
+            dw = decode_interleaved(Td)
+            dq_ = dev_bf16(dw.qkv)
+            dp = torch.from_numpy(dw.positions).to(dev)
+            dwq_, dwk_ = dev_bf16(dw.q_norm_w), dev_bf16(dw.k_norm_w)
+            o = (torch.empty((Td, 128, 64), dtype=torch.bfloat16, device=dev),
+                 torch.empty((Td, 16, 64), dtype=torch.bfloat16, device=dev),
+                 torch.empty((Td, 16, 64), dtype=torch.bfloat16, device=dev))
+            dk_ = dict(kind="interleaved", n_kv=16, q_per_kv=8, head_dim=64, eps=1e-6, theta=5e5)
+            side = torch.cuda.Stream()
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                for _ in range(3):
+                    qk.forward(dq_, dp, dwq_, dwk_, out=o, **dk_)
+            stream.wait_stream(side)
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 for _ in range(CALLS):
-                    qk.forward_latent_paged(rows, lp, lwk, bt, pool, tokens_per_req=lw.tokens_per_req)
+                    qk.forward(dq_, dp, dwq_, dwk_, out=o, **dk_)
             for _ in range(5):
                 g.replay()
             n = 20
@@ -651,20 +627,44 @@ def main():
                 g.replay()
             e1.record(stream)
             torch.cuda.synchronize()
-            extras["mla_latent_paged_B4xT16_us"] = round(e0.elapsed_time(e1) / (n * CALLS) * 1e3, 2)
-            del pool, g
+            extras[f"decode_T{Td}_us"] = round(e0.elapsed_time(e1) / (n * CALLS) * 1e3, 2)
+            del g
+
+    # ------------------------------------------------------------ MLA latent rows into the paged pool
+    if "mla" in legs:
+        lw = latent_paged()
+        rows, lp, lwk = dev_bf16(lw.qkv), torch.from_numpy(lw.positions).to(dev), dev_bf16(lw.k_norm_w)
+        bt = torch.from_numpy(lw.block_table).to(dev)
+        pool = torch.zeros((lw.num_pages, lw.page_size, 576), dtype=torch.bfloat16, device=dev)
+        for _ in range(3):
+            qk.forward_latent_paged(rows, lp, lwk, bt, pool, tokens_per_req=lw.tokens_per_req)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(CALLS):
+                qk.forward_latent_paged(rows, lp, lwk, bt, pool, tokens_per_req=lw.tokens_per_req)
+        for _ in range(5):
+            g.replay()
+        n = 20
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        extras["mla_latent_paged_B4xT16_us"] = round(e0.elapsed_time(e1) / (n * CALLS) * 1e3, 2)
+        del pool, g
 
     # ------------------------------------------------------------ MLA drafter layers: kv path beside q path
     if "drafter" in legs:
-            extras["mla_drafter"] = drafter_extras(dev_bf16, stream)
+        extras["mla_drafter"] = drafter_extras(dev_bf16, stream)
 
     # ------------------------------------------------------------ per-head Newton-Schulz on the fused weight
     if "muon" in legs:
-            extras["muon_newton_schulz"] = muon_extras(stream)
+        extras["muon_newton_schulz"] = muon_extras(stream)
 
     # ------------------------------------------------------------ QKV projection with the region in its epilogue
     if "proj" in legs:
-            extras["fused_qkv_projection"] = proj_extras(stream)
+        extras["fused_qkv_projection"] = proj_extras(stream)
 
     out = {
         "metric": METRIC,
